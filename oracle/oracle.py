@@ -1,0 +1,169 @@
+"""ctypes face of the fp64 CPU oracle (oracle/gdn_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the bench's
+CPU-baseline leg are the only users.  The mixer library and its Python binding
+never import this module, and this module imports nothing from them.
+
+``build()`` compiles ``liboracle.so`` next to this file with gcc (-O2, OpenMP);
+``load()`` builds it if it is missing.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_d = C.POINTER(C.c_double)
+_u16 = C.POINTER(C.c_uint16)
+_f32 = C.POINTER(C.c_float)
+_i32 = C.POINTER(C.c_int32)
+
+
+def build() -> str:
+    """Compile the oracle (always); returns the library path."""
+    tmp = _LIB + ".tmp"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-std=c11", "-Wall", "-shared", "-fPIC",
+                    "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load():
+    """Load the oracle library (building it when stale).  GDN_ORACLE_LIB names
+    another build of the same source, used by the planted-mistake test."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = os.environ.get("GDN_ORACLE_LIB")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+    lib = C.CDLL(path)
+    core_sig = [C.c_int, C.c_int, C.c_int, _d, _d, _d, _d, _d, _d, _d]
+    lib.oracle_core_sequential.argtypes = core_sig
+    lib.oracle_core_bruteforce.argtypes = core_sig
+    lib.oracle_core_chunked.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, _d, _d, _d, _d, _d, _d, _d]
+    lib.oracle_conv_silu_channel.argtypes = [C.c_int, _d, _d, _d, _d]
+    lib.oracle_conv_silu_channel.restype = None
+    lib.oracle_l2norm.argtypes = [C.c_int, _d, C.c_double, C.c_double, _d]
+    lib.oracle_l2norm.restype = None
+    lib.oracle_gated_rmsnorm.argtypes = [C.c_int, _d, _d, _d, C.c_double, _d]
+    lib.oracle_gated_rmsnorm.restype = None
+    lib.oracle_prefill.argtypes = [C.c_int] * 8 + [C.c_double, C.c_double] + [
+        _u16, _u16, _u16, _f32, _f32, _u16, _u16, _u16, _f32, _u16, C.c_int, _i32, _d, _d, _u16, C.c_int]
+    lib.oracle_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _p(a, t):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def num_threads() -> int:
+    return int(load().oracle_num_threads())
+
+
+def _core(fn, q, k, v, g, beta, S0, *extra):
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if S0 is None else _f64(S0).copy()
+    o = np.zeros((T, dv))
+    rc = fn(T, dk, dv, *extra, _p(q, _d), _p(k, _d), _p(v, _d), _p(g, _d), _p(beta, _d), _p(S, _d), _p(o, _d))
+    if rc != 0:
+        raise RuntimeError(f"oracle core failed: {rc}")
+    return o, S
+
+
+def core_sequential(q, k, v, g, beta, S0=None):
+    """Token-by-token recurrence on normalised k and scaled q: returns (o [T,dv], S [dk,dv])."""
+    return _core(load().oracle_core_sequential, q, k, v, g, beta, S0)
+
+
+def core_chunked(q, k, v, g, beta, S0=None, C=64):
+    """Chunked (unit lower-triangular) form of the same recurrence."""
+    lib = load()
+
+    def fn(T, dk, dv, *rest):
+        return lib.oracle_core_chunked(T, dk, dv, C, *rest)
+    return _core(fn, q, k, v, g, beta, S0)
+
+
+def core_bruteforce(q, k, v, g, beta, S0=None):
+    """Explicit product expansion of the recurrence (tiny T only)."""
+    return _core(load().oracle_core_bruteforce, q, k, v, g, beta, S0)
+
+
+def conv_silu_channel(x, w4, hist3=None):
+    x, w4 = _f64(x), _f64(w4)
+    h = None if hist3 is None else _f64(hist3)
+    u = np.zeros_like(x)
+    load().oracle_conv_silu_channel(len(x), _p(x, _d), _p(w4, _d), _p(h, _d), _p(u, _d))
+    return u
+
+
+def l2norm(x, eps=1e-6, scale=1.0):
+    x = _f64(x)
+    out = np.zeros_like(x)
+    load().oracle_l2norm(len(x), _p(x, _d), eps, scale, _p(out, _d))
+    return out
+
+
+def gated_rmsnorm(o, z, w, eps=1e-6):
+    o, z, w = _f64(o), _f64(z), _f64(w)
+    y = np.zeros_like(o)
+    load().oracle_gated_rmsnorm(len(o), _p(o, _d), _p(z, _d), _p(w, _d), eps, _p(y, _d))
+    return y
+
+
+def prefill(inp: dict, B: int, T: int, Hk: int, Hv: int, conv: bool, norm: bool,
+            chains=None, eps_l2=1e-6, eps_norm=1e-6, threads=0, want_conv_state=True,
+            state_in=None, conv_state_in=None, dk=128, dv=128):
+    """The whole hot path for the listed chains (b*Hv + h; None = all).
+
+    ``inp`` holds the boundary-format arrays of gdn_inputs.make_inputs (q, k, v,
+    z, g, beta, conv_w, norm_w; bf16 as uint16).  ``state_in`` / ``conv_state_in``
+    override inp['state'] / inp['conv_state'] when given.
+    Returns (y [n, T, dv] fp64, state [n, dk, dv] fp64, conv_state_out [B,3,Cc] uint16 or None).
+    """
+    lib = load()
+    if state_in is None:
+        state_in = inp.get("state")
+    if conv_state_in is None:
+        conv_state_in = inp.get("conv_state")
+    ch = None if chains is None else np.ascontiguousarray(chains, dtype=np.int32)
+    n = B * Hv if ch is None else len(ch)
+    y = np.empty((n, T, dv))
+    st = np.empty((n, dk, dv))
+    Cc = 2 * Hk * dk + Hv * dv
+    cs_out = np.zeros((B, 3, Cc), dtype=np.uint16) if (want_conv_state and conv) else None
+
+    def c16(a):
+        return None if a is None else np.ascontiguousarray(a, dtype=np.uint16)
+
+    def c32(a):
+        return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+    q, k, v, z = c16(inp["q"]), c16(inp["k"]), c16(inp["v"]), c16(inp.get("z") if norm else None)
+    g, beta = c32(inp["g"]), c32(inp["beta"])
+    cw, nw = c16(inp.get("conv_w") if conv else None), c16(inp.get("norm_w") if norm else None)
+    s_in, cs_in = c32(state_in), c16(conv_state_in if conv else None)
+    rc = lib.oracle_prefill(B, T, Hk, Hv, dk, dv, 4 if conv else 0, 1 if norm else 0, eps_l2, eps_norm,
+                            _p(q, _u16), _p(k, _u16), _p(v, _u16), _p(g, _f32), _p(beta, _f32),
+                            _p(z, _u16), _p(cw, _u16), _p(nw, _u16), _p(s_in, _f32), _p(cs_in, _u16),
+                            n, _p(ch, _i32), _p(y, _d), _p(st, _d), _p(cs_out, _u16), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill failed: {rc}")
+    return y, st, cs_out
