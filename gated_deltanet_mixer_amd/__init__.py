@@ -1,0 +1,110 @@
+"""Python binding of the Gated DeltaNet mixer C ABI (include/gdn.h).
+
+Argument marshalling only: every step of the mixer runs in the HIP kernels of
+libgdn.so.  Tensors are torch tensors on the GPU (bf16 tensors may be
+torch.bfloat16 or 16-bit integer views of the same bits); ``None`` passes a
+NULL pointer.  Work is enqueued on torch's current stream unless ``stream`` is
+given.  A non-zero status raises GdnError.  The import fails loudly when
+libgdn.so has not been built (``python -m gated_deltanet_mixer_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+GDN_OK = 0
+GDN_EINVAL = -1
+GDN_EUNSUPPORTED = -2
+GDN_EHIP = -3
+GDN_EWORKSPACE = -4
+GDN_NO_NORM = 1
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {gdn_status_string(status)} (status {status})")
+        self.status = status
+
+
+class gdn_shape(C.Structure):
+    _fields_ = [("B", C.c_int32), ("T", C.c_int32), ("Hk", C.c_int32), ("Hv", C.c_int32),
+                ("Dk", C.c_int32), ("Dv", C.c_int32), ("conv_width", C.c_int32), ("flags", C.c_uint32),
+                ("eps_l2", C.c_float), ("eps_norm", C.c_float)]
+
+
+def make_shape(B: int, T: int, Hk: int, Hv: int, conv: bool = True, norm: bool = True,
+               eps_l2: float = 1e-6, eps_norm: float = 1e-6, Dk: int = 128, Dv: int = 128) -> gdn_shape:
+    return gdn_shape(B, T, Hk, Hv, Dk, Dv, 4 if conv else 0, 0 if norm else GDN_NO_NORM, eps_l2, eps_norm)
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gated_deltanet_mixer_amd.build`")
+_lib = C.CDLL(LIB_PATH)
+_vp = C.c_void_p
+_sp = C.POINTER(gdn_shape)
+_lib.gdn_status_string.argtypes = [C.c_int]
+_lib.gdn_status_string.restype = C.c_char_p
+_lib.gdn_state_init.argtypes = [_sp, _vp, _vp, _vp]
+_lib.gdn_prefill_workspace_size.argtypes = [_sp, C.POINTER(C.c_size_t)]
+_lib.gdn_prefill.argtypes = [_sp] + [_vp] * 14 + [C.c_size_t, _vp]
+_lib.gdn_decode_step.argtypes = [_sp] + [_vp] * 12
+
+EXPORTED = ("gdn_state_init", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
+            "gdn_status_string")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != GDN_OK:
+        raise GdnError(fn, rc)
+
+
+def gdn_status_string(status: int) -> str:
+    return _lib.gdn_status_string(status).decode()
+
+
+def gdn_state_init(shape: gdn_shape, state, conv_state=None, stream=None) -> None:
+    _check("gdn_state_init", _lib.gdn_state_init(C.byref(shape), _ptr(state), _ptr(conv_state), _stream(stream)))
+
+
+def gdn_prefill_workspace_size(shape: gdn_shape) -> int:
+    n = C.c_size_t(0)
+    _check("gdn_prefill_workspace_size", _lib.gdn_prefill_workspace_size(C.byref(shape), C.byref(n)))
+    return int(n.value)
+
+
+def gdn_prefill(shape: gdn_shape, q, k, v, g, beta, z, conv_w, norm_w, state_in, conv_state_in,
+                o, state_out, conv_state_out, workspace, workspace_bytes: int | None = None,
+                stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.gdn_prefill(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
+                          _ptr(conv_w), _ptr(norm_w), _ptr(state_in), _ptr(conv_state_in), _ptr(o),
+                          _ptr(state_out), _ptr(conv_state_out), _ptr(workspace), int(workspace_bytes),
+                          _stream(stream))
+    _check("gdn_prefill", rc)
+
+
+def gdn_decode_step(shape: gdn_shape, q, k, v, g, beta, z, conv_w, norm_w, state, conv_state, o,
+                    stream=None) -> None:
+    rc = _lib.gdn_decode_step(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
+                              _ptr(conv_w), _ptr(norm_w), _ptr(state), _ptr(conv_state), _ptr(o),
+                              _stream(stream))
+    _check("gdn_decode_step", rc)

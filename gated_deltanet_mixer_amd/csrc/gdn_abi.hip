@@ -1,0 +1,190 @@
+// gdn_abi.hip -- the C ABI of include/gdn.h: argument checks, then launches.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// enqueues nothing and needs no device.
+#include <stdint.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kD = 128;
+
+__global__ void fill_zero_kernel(uint4 *p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// Shape checks shared by every entry point.  T is checked only when `use_T`.
+int check_shape(const gdn_shape *s, bool use_T) {
+    if (!s) return GDN_EINVAL;
+    if (s->B < 1 || s->Hk < 1 || s->Hv < 1 || (use_T && s->T < 1)) return GDN_EINVAL;
+    if (s->Hv % s->Hk != 0) return GDN_EINVAL;
+    if (s->Dk != kD || s->Dv != kD) return GDN_EUNSUPPORTED;
+    if (s->conv_width != 0 && s->conv_width != 4) return GDN_EUNSUPPORTED;
+    if (s->flags & ~GDN_NO_NORM) return GDN_EINVAL;
+    if (!(s->eps_l2 >= 0.0f) || !(s->eps_norm >= 0.0f)) return GDN_EINVAL;
+    // sizes must fit the kernels' 32-bit token and head indices
+    if ((long long)s->B * s->Hv * kD > 0x7fffffffLL || (use_T && (long long)s->T * kD > 0x7fffffffLL))
+        return GDN_EINVAL;
+    return GDN_OK;
+}
+
+size_t conv_channels(const gdn_shape *s) { return (size_t)2 * s->Hk * kD + (size_t)s->Hv * kD; }
+
+} // namespace
+} // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+const char *gdn_status_string(int status) {
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument (null or misaligned pointer, bad size, or overlapping buffers)";
+    case GDN_EUNSUPPORTED: return "unsupported shape (head width must be 128, conv width 0 or 4)";
+    case GDN_EHIP: return "a HIP call or kernel launch failed";
+    case GDN_EWORKSPACE: return "workspace too small";
+    default: return "unknown status";
+    }
+}
+
+int gdn_state_init(const gdn_shape *shape, float *state, uint16_t *conv_state, void *stream) {
+    int rc = check_shape(shape, false);
+    if (rc) return rc;
+    if (!state || !aligned(state, 16) || (conv_state && !aligned(conv_state, 16))) return GDN_EINVAL;
+    if (conv_state && shape->conv_width == 0) return GDN_EINVAL;
+    const size_t n_state = (size_t)shape->B * shape->Hv * kD * kD;
+    const size_t n_conv = conv_state ? (size_t)shape->B * 3 * conv_channels(shape) : 0;
+    return launch_state_init(state, n_state, conv_state, n_conv, static_cast<hipStream_t>(stream)) ? GDN_EHIP
+                                                                                                   : GDN_OK;
+}
+
+int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes) {
+    int rc = check_shape(shape, true);
+    if (rc) return rc;
+    if (!bytes) return GDN_EINVAL;
+    PrefillPlan plan;
+    plan_prefill(shape->B, shape->T, shape->Hk, shape->Hv, &plan);
+    *bytes = plan.qk_bytes + plan.mbox_bytes;
+    return GDN_OK;
+}
+
+int gdn_prefill(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
+                const float *state_in, const uint16_t *conv_state_in, uint16_t *o, float *state_out,
+                uint16_t *conv_state_out, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_shape(s, true);
+    if (rc) return rc;
+    const bool norm = !(s->flags & GDN_NO_NORM);
+    const bool conv = s->conv_width == 4;
+    if (!q || !k || !v || !g || !beta || !o || !state_out || !workspace) return GDN_EINVAL;
+    if (norm && (!z || !norm_w)) return GDN_EINVAL;
+    if (conv != (conv_w != nullptr)) return GDN_EINVAL;
+    if (!conv && (conv_state_in || conv_state_out)) return GDN_EINVAL;
+    const void *a16[] = {q, k, v, z, conv_w, norm_w, state_in, conv_state_in, o, state_out, conv_state_out, workspace};
+    for (const void *p : a16)
+        if (p && !aligned(p, 16)) return GDN_EINVAL;
+    if (!aligned(g, 4) || !aligned(beta, 4)) return GDN_EINVAL;
+
+    const size_t B = s->B, T = s->T, Hk = s->Hk, Hv = s->Hv, Cc = conv_channels(s);
+    const size_t nqk = B * T * Hk * kD * 2, nv = B * T * Hv * kD * 2, ngb = B * T * Hv * 4;
+    const size_t nst = B * Hv * kD * kD * 4, ncs = B * 3 * Cc * 2;
+    const size_t nw = conv ? Cc * 4 * 2 : 0, nn = norm ? kD * 2 : 0;
+    const struct {
+        const void *p;
+        size_t n;
+    } inputs[] = {{q, nqk}, {k, nqk}, {v, nv}, {g, ngb}, {beta, ngb}, {norm ? z : nullptr, nv},
+                  {conv_w, nw}, {norm_w, nn}, {state_in, nst}, {conv_state_in, ncs}};
+    for (const auto &in : inputs)
+        if (overlap(o, nv, in.p, in.n) || overlap(workspace, workspace_bytes, in.p, in.n)) return GDN_EINVAL;
+    if (overlap(conv_state_out, ncs, conv_state_in, ncs)) return GDN_EINVAL;
+    // state_out may be state_in exactly, but must not partly overlap anything else
+    if (state_out != state_in && overlap(state_out, nst, state_in, nst)) return GDN_EINVAL;
+    for (const auto &in : inputs)
+        if (in.p != state_in && overlap(state_out, nst, in.p, in.n)) return GDN_EINVAL;
+    if (overlap(o, nv, state_out, nst) || overlap(o, nv, conv_state_out, ncs) ||
+        overlap(workspace, workspace_bytes, o, nv) || overlap(workspace, workspace_bytes, state_out, nst) ||
+        overlap(workspace, workspace_bytes, conv_state_out, ncs) || overlap(state_out, nst, conv_state_out, ncs))
+        return GDN_EINVAL;
+
+    PrefillPlan plan;
+    plan_prefill(s->B, s->T, s->Hk, s->Hv, &plan);
+    if (workspace_bytes < plan.qk_bytes + plan.mbox_bytes) return GDN_EWORKSPACE;
+
+    PrefillParams p;
+    p.q = q; p.k = k; p.v = v; p.z = norm ? z : nullptr; p.conv_w = conv_w; p.norm_w = norm ? norm_w : nullptr;
+    p.conv_state_in = conv_state_in; p.g = g; p.beta = beta; p.state_in = state_in;
+    p.o = o; p.conv_state_out = conv_state_out; p.state_out = state_out; p.workspace = workspace;
+    p.B = s->B; p.T = s->T; p.Hk = s->Hk; p.Hv = s->Hv; p.conv_width = s->conv_width; p.norm = norm;
+    p.eps_l2 = s->eps_l2; p.eps_norm = s->eps_norm;
+    return launch_prefill(p, plan, static_cast<hipStream_t>(stream)) ? GDN_EHIP : GDN_OK;
+}
+
+int gdn_decode_step(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                    const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
+                    float *state, uint16_t *conv_state, uint16_t *o, void *stream) {
+    int rc = check_shape(s, false);
+    if (rc) return rc;
+    const bool norm = !(s->flags & GDN_NO_NORM);
+    const bool conv = s->conv_width == 4;
+    if (!q || !k || !v || !g || !beta || !o || !state) return GDN_EINVAL;
+    if (norm && (!z || !norm_w)) return GDN_EINVAL;
+    if (conv != (conv_w != nullptr) || conv != (conv_state != nullptr)) return GDN_EINVAL;
+    const void *a16[] = {q, k, v, z, conv_w, norm_w, state, conv_state, o};
+    for (const void *p : a16)
+        if (p && !aligned(p, 16)) return GDN_EINVAL;
+    if (!aligned(g, 4) || !aligned(beta, 4)) return GDN_EINVAL;
+    if (s->Hv / s->Hk > 64) return GDN_EUNSUPPORTED;  // the r value heads' conv outputs must fit one workgroup's LDS
+
+    const size_t B = s->B, Hk = s->Hk, Hv = s->Hv, Cc = conv_channels(s);
+    const size_t nqk = B * Hk * kD * 2, nv = B * Hv * kD * 2, ngb = B * Hv * 4;
+    const size_t nst = B * Hv * kD * kD * 4, ncs = B * 3 * Cc * 2;
+    const size_t nw = conv ? Cc * 4 * 2 : 0, nn = norm ? kD * 2 : 0;
+    const struct {
+        const void *p;
+        size_t n;
+    } ro[] = {{q, nqk}, {k, nqk}, {v, nv}, {g, ngb}, {beta, ngb}, {norm ? z : nullptr, nv},
+              {conv_w, nw}, {norm_w, nn}};
+    for (const auto &in : ro)
+        if (overlap(o, nv, in.p, in.n) || overlap(state, nst, in.p, in.n) || overlap(conv_state, ncs, in.p, in.n))
+            return GDN_EINVAL;
+    if (overlap(o, nv, state, nst) || overlap(o, nv, conv_state, ncs) || overlap(state, nst, conv_state, ncs))
+        return GDN_EINVAL;
+
+    DecodeParams p;
+    p.q = q; p.k = k; p.v = v; p.z = norm ? z : nullptr; p.conv_w = conv_w; p.norm_w = norm ? norm_w : nullptr;
+    p.g = g; p.beta = beta; p.state = state; p.conv_state = conv_state; p.o = o;
+    p.B = s->B; p.Hk = s->Hk; p.Hv = s->Hv; p.conv_width = s->conv_width; p.norm = norm;
+    p.eps_l2 = s->eps_l2; p.eps_norm = s->eps_norm;
+    return launch_decode(p, static_cast<hipStream_t>(stream)) ? GDN_EHIP : GDN_OK;
+}
+
+} // extern "C"
+
+namespace gdn {
+int launch_state_init(float *state, size_t n_state, uint16_t *conv_state, size_t n_conv, hipStream_t stream) {
+    const size_t n16s = n_state * sizeof(float) / 16;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, stream, reinterpret_cast<uint4 *>(state), n16s);
+    if (hipGetLastError() != hipSuccess) return -1;
+    if (conv_state && n_conv) {
+        const size_t n16c = n_conv * sizeof(uint16_t) / 16;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, reinterpret_cast<uint4 *>(conv_state),
+                           n16c);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
+    return 0;
+}
+} // namespace gdn

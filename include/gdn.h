@@ -1,0 +1,145 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet token-mixer hot path on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The mixer computes, per sequence b, value head h and token t:
+ *
+ *   u     = silu(sum_{j<4} w[c,j] x[t+j-3,c])  on the q, k and v channels
+ *           ("Qwen3.8-27B" model spec, compute-graph node gdn.conv; "How
+ *           Qwen3.5 works" §9.3);
+ *   k^    = u_k / sqrt(sum u_k^2 + eps_l2),  q^ = u_q / sqrt(sum u_q^2 + eps_l2)
+ *           / sqrt(Dk)  ("How Qwen3.5 works" §9.4; model spec node gdn.core),
+ *           value head h reading key head h / (Hv/Hk);
+ *   S_t   = e^{g_t} S_{t-1} + k^ d^T,  d = beta_t (v_t - e^{g_t} S_{t-1}^T k^),
+ *   o_t   = S_t^T q^   ("How Qwen3.5 works" §9.6: decay, predict, correct,
+ *           read; the model spec's gdn.core writes the same rule transposed);
+ *   y_t   = w * o_t / sqrt(mean(o_t^2) + eps_norm) * silu(z_t)
+ *           (model spec node gdn.norm; "How Qwen3.5 works" §9.9).
+ *
+ * State layout.  The recurrent state is fp32 [B][Hv][Dk][Dv], K-major: element
+ * [b][h][i][j] is key dimension i, value dimension j (the orientation
+ * S in R^{dk x dv} of "How Qwen3.5 works" §9.1).  The conv state is bf16
+ * [B][3][Cc], Cc = 2*Hk*Dk + Hv*Dv: the raw (pre-conv) inputs of the last
+ * three tokens, oldest first, channels ordered q heads, k heads, v heads
+ * ("How Qwen3.5 works" §13.1/§13.3: the decode step shifts this window).
+ *
+ * Conventions for every call.
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous; bf16
+ *    tensors are passed as uint16_t bit patterns.  The caller owns every
+ *    buffer.  The library allocates nothing and never synchronises.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it; results are visible once the caller syncs it.
+ *  - Every argument is checked on the host before any HIP call; a failed
+ *    check returns a negative status and enqueues nothing.  No exception
+ *    crosses the ABI and the library never prints.
+ *  - Pointers to bf16 tensors and to the state must be 16-byte aligned; g and
+ *    beta 4-byte aligned.
+ *  - Supported: Dk = Dv = 128, Hv a multiple of Hk, conv_width 0 or 4.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GDN_OK 0
+#define GDN_EINVAL (-1)      /* null or misaligned pointer, bad size, aliasing */
+#define GDN_EUNSUPPORTED (-2) /* a head width other than 128, a conv width other than 0/4 */
+#define GDN_EHIP (-3)        /* a HIP call or kernel launch failed */
+#define GDN_EWORKSPACE (-4)  /* workspace too small */
+
+/* flags */
+#define GDN_NO_NORM 1u /* return the raw read-out o instead of the gated RMSNorm (z, norm_w unused) */
+
+typedef struct gdn_shape {
+    int32_t B;          /* sequences, >= 1 */
+    int32_t T;          /* tokens per sequence, >= 1 (gdn_decode_step ignores it) */
+    int32_t Hk;         /* key / query heads, >= 1 */
+    int32_t Hv;         /* value heads, a multiple of Hk */
+    int32_t Dk;         /* key head width: must be 128 */
+    int32_t Dv;         /* value head width: must be 128 */
+    int32_t conv_width; /* 0: q, k, v enter the rule as given (no conv, no SiLU); 4: width-4 causal conv + SiLU */
+    uint32_t flags;     /* GDN_NO_NORM or 0 */
+    float eps_l2;       /* eps inside the q/k L2-norm root (1e-6 on the pages) */
+    float eps_norm;     /* eps of the gated RMSNorm (1e-6 on the pages) */
+} gdn_shape;
+
+/*
+ * Zero the recurrent state [B][Hv][Dk][Dv] fp32 and, when conv_state is not
+ * NULL, the conv state [B][3][Cc] bf16: the state before the first token
+ * ("How Qwen3.5 works" §9.8 starts from S_0 = 0; §9.10's reference loop
+ * allocates zeros when no state is given).
+ */
+int gdn_state_init(const gdn_shape *shape, float *state, uint16_t *conv_state, void *stream);
+
+/*
+ * Bytes of device workspace gdn_prefill needs for `shape` (written to *bytes).
+ * The workspace holds the normalised q/k operands (fp16, B*T*Hk*2*Dk values)
+ * and the per-row sums of squares that workgroups sharing one head exchange
+ * for the gated RMSNorm.
+ */
+int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
+
+/*
+ * Prefill: run T tokens of every sequence through the mixer, chunked into
+ * blocks of 64 tokens ("How Qwen3.5 works" §9.11: the unit lower-triangular
+ * chunk form of the same recurrence; a partial last chunk is allowed).
+ *
+ *  q, k           [B][T][Hk][128] bf16
+ *  v, z           [B][T][Hv][128] bf16 (z may be NULL iff GDN_NO_NORM)
+ *  g, beta        [B][T][Hv] fp32: log-decay (alpha = e^g) and write strength
+ *  conv_w         [Cc][4] bf16, tap 3 multiplies the current token (NULL iff conv_width == 0)
+ *  norm_w         [128] bf16, the gated-norm weight, applied as w (NULL iff GDN_NO_NORM)
+ *  state_in       [B][Hv][128][128] fp32, or NULL for zeros
+ *  conv_state_in  [B][3][Cc] bf16, or NULL for zeros (must be NULL when conv_width == 0)
+ *  o              [B][T][Hv][128] bf16 output (round to nearest even)
+ *  state_out      [B][Hv][128][128] fp32 output; may be the same buffer as state_in
+ *  conv_state_out [B][3][Cc] bf16, the raw inputs of the last three tokens, or
+ *                 NULL; must not overlap conv_state_in
+ *  workspace      device memory of at least gdn_prefill_workspace_size() bytes.
+ *                 It must be zero-filled before its first use; every call that
+ *                 completes leaves its exchange area zeroed again.  Calls that
+ *                 run concurrently must not share a workspace.
+ *
+ * `o` must not overlap any input.  Returns GDN_OK once the work is enqueued.
+ */
+int gdn_prefill(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
+                const uint16_t *v, const float *g, const float *beta, const uint16_t *z,
+                const uint16_t *conv_w, const uint16_t *norm_w, const float *state_in,
+                const uint16_t *conv_state_in, uint16_t *o, float *state_out,
+                uint16_t *conv_state_out, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/*
+ * One decode step: one new token per sequence, updating the recurrent state
+ * and the conv window in place ("How Qwen3.5 works" §13.3: each linear layer
+ * shifts its conv state and takes one recurrent step; the state is
+ * overwritten, nothing grows).
+ *
+ *  q, k        [B][Hk][128] bf16;  v, z [B][Hv][128] bf16 (z NULL iff GDN_NO_NORM)
+ *  g, beta     [B][Hv] fp32
+ *  conv_w      [Cc][4] bf16 (NULL iff conv_width == 0);  norm_w [128] bf16
+ *  state       [B][Hv][128][128] fp32, read and overwritten in place
+ *  conv_state  [B][3][Cc] bf16, read and shifted in place (NULL iff conv_width == 0)
+ *  o           [B][Hv][128] bf16 output
+ *
+ * shape->T is ignored.  `o` must not overlap any input.
+ */
+int gdn_decode_step(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
+                    const uint16_t *v, const float *g, const float *beta, const uint16_t *z,
+                    const uint16_t *conv_w, const uint16_t *norm_w, float *state,
+                    uint16_t *conv_state, uint16_t *o, void *stream);
+
+/* A static, NUL-terminated description of a status code. */
+const char *gdn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,159 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/gdn.h declares, and rejects bad arguments before any HIP call (so
+these run without a GPU)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+gdn = pytest.importorskip("gated_deltanet_mixer_amd")
+
+FAKE = 1 << 40  # a 256-byte aligned "device address"; never dereferenced by a rejected call
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(
+        ["gdn_decode_step", "gdn_prefill", "gdn_prefill_workspace_size", "gdn_state_init", "gdn_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", out))
+    for fn in declared_functions():
+        assert fn in exported, fn
+        assert hasattr(gdn._lib, fn)
+
+
+def test_binding_names_match_the_abi():
+    for fn in declared_functions():
+        assert callable(getattr(gdn, fn)), fn
+
+
+def test_status_strings():
+    for code in (gdn.GDN_OK, gdn.GDN_EINVAL, gdn.GDN_EUNSUPPORTED, gdn.GDN_EHIP, gdn.GDN_EWORKSPACE):
+        s = gdn.gdn_status_string(code)
+        assert s and s != "unknown status"
+    assert gdn.gdn_status_string(12345) == "unknown status"
+
+
+def _prefill_args(shape, **over):
+    """Arguments of a well-formed prefill on fake, disjoint device addresses."""
+    B, T, Hk, Hv = shape.B, shape.T, shape.Hk, shape.Hv
+    base = FAKE
+    sizes = dict(q=B * T * Hk * 256, k=B * T * Hk * 256, v=B * T * Hv * 256, g=B * T * Hv * 4,
+                 beta=B * T * Hv * 4, z=B * T * Hv * 256, conv_w=(2 * Hk + Hv) * 128 * 8, norm_w=256,
+                 state_in=B * Hv * 65536, conv_state_in=B * 3 * (2 * Hk + Hv) * 256, o=B * T * Hv * 256,
+                 state_out=B * Hv * 65536, conv_state_out=B * 3 * (2 * Hk + Hv) * 256)
+    args = {}
+    for n, sz in sizes.items():
+        args[n] = base
+        base += ((sz + MB - 1) // MB + 1) * MB
+    args["workspace"] = base
+    if "workspace_bytes" not in over:
+        args["workspace_bytes"] = gdn.gdn_prefill_workspace_size(shape)
+    args.update(over)
+    return args
+
+
+def _call_prefill(shape, **over):
+    a = _prefill_args(shape, **over)
+    return gdn._lib.gdn_prefill(C.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], a["z"], a["conv_w"],
+                                a["norm_w"], a["state_in"], a["conv_state_in"], a["o"], a["state_out"],
+                                a["conv_state_out"], a["workspace"], a["workspace_bytes"], None)
+
+
+def _shape(**kw):
+    s = dict(B=2, T=100, Hk=2, Hv=6, conv=True, norm=True)
+    s.update(kw)
+    return gdn.make_shape(**s)
+
+
+def test_workspace_size_scales_with_tokens():
+    a = gdn.gdn_prefill_workspace_size(_shape(T=64))
+    b = gdn.gdn_prefill_workspace_size(_shape(T=6400))
+    assert b > a > 0
+    assert b >= 2 * 6400 * 2 * 2 * 128 * 2  # fp16 q/k operands
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("B", 0, gdn.GDN_EINVAL), ("T", 0, gdn.GDN_EINVAL), ("Hv", 5, gdn.GDN_EINVAL),
+    ("Dk", 64, gdn.GDN_EUNSUPPORTED), ("Dv", 256, gdn.GDN_EUNSUPPORTED),
+    ("conv_width", 3, gdn.GDN_EUNSUPPORTED), ("flags", 8, gdn.GDN_EINVAL),
+])
+def test_bad_shapes_rejected(field, value, code):
+    s = _shape()
+    setattr(s, field, value)
+    n = C.c_size_t(0)
+    assert gdn._lib.gdn_prefill_workspace_size(C.byref(s), C.byref(n)) == code
+    assert _call_prefill(s, workspace_bytes=1 << 40) == code
+
+
+def test_null_and_misaligned_pointers_rejected():
+    s = _shape()
+    assert gdn._lib.gdn_prefill(None, *([FAKE] * 14), 1 << 30, None) == gdn.GDN_EINVAL
+    for name in ("q", "k", "v", "g", "beta", "o", "state_out", "workspace"):
+        assert _call_prefill(s, **{name: None}) == gdn.GDN_EINVAL, name
+    assert _call_prefill(s, z=None) == gdn.GDN_EINVAL            # norm on needs z
+    assert _call_prefill(s, conv_w=None) == gdn.GDN_EINVAL       # conv on needs weights
+    assert _call_prefill(s, q=FAKE + 8) == gdn.GDN_EINVAL        # 16-byte alignment
+    assert _call_prefill(s, g=FAKE + 2) == gdn.GDN_EINVAL        # 4-byte alignment
+
+
+def test_overlaps_rejected():
+    s = _shape()
+    a = _prefill_args(s)
+    assert _call_prefill(s, o=a["q"]) == gdn.GDN_EINVAL
+    assert _call_prefill(s, conv_state_out=a["conv_state_in"]) == gdn.GDN_EINVAL
+    assert _call_prefill(s, workspace=a["v"]) == gdn.GDN_EINVAL
+    assert _call_prefill(s, state_out=a["state_in"] + 1024) == gdn.GDN_EINVAL
+
+
+def test_small_workspace_rejected_last():
+    s = _shape()
+    ws = gdn.gdn_prefill_workspace_size(s)
+    assert _call_prefill(s, workspace_bytes=ws - 1) == gdn.GDN_EWORKSPACE
+
+
+def test_conv_state_without_conv_rejected():
+    s = _shape(conv=False)
+    assert _call_prefill(s, conv_w=None) == gdn.GDN_EINVAL  # conv_state_in/out given without conv
+
+
+def test_decode_rejects_bad_arguments():
+    s = _shape()
+    # q, k, v, g, beta, z, conv_w, norm_w, state, conv_state, o
+    ok = [FAKE + i * (64 * MB) for i in range(11)]
+    f = gdn._lib.gdn_decode_step
+    assert f(None, *ok, None) == gdn.GDN_EINVAL
+    bad = list(ok)
+    bad[0] = FAKE + 4
+    assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
+    bad = list(ok)
+    bad[9] = None  # conv state with conv on
+    assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
+    bad = list(ok)
+    bad[10] = ok[0]  # o on top of q
+    assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
+    s2 = _shape(Hk=1, Hv=65)
+    assert f(C.byref(s2), *ok, None) == gdn.GDN_EUNSUPPORTED
+
+
+def test_state_init_rejects_bad_arguments():
+    s = _shape()
+    f = gdn._lib.gdn_state_init
+    assert f(C.byref(s), None, None, None) == gdn.GDN_EINVAL
+    assert f(C.byref(s), FAKE + 4, None, None) == gdn.GDN_EINVAL
+    s0 = _shape(conv=False)
+    assert f(C.byref(s0), FAKE, FAKE + MB * 512, None) == gdn.GDN_EINVAL
