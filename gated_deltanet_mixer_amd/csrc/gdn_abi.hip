@@ -78,7 +78,7 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes) {
     if (!bytes) return GDN_EINVAL;
     PrefillPlan plan;
     plan_prefill(shape->B, shape->T, shape->Hk, shape->Hv, &plan);
-    *bytes = plan.qk_bytes + plan.mbox_bytes;
+    *bytes = plan.total_bytes;
     return GDN_OK;
 }
 
@@ -122,7 +122,7 @@ int gdn_prefill(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const 
 
     PrefillPlan plan;
     plan_prefill(s->B, s->T, s->Hk, s->Hv, &plan);
-    if (workspace_bytes < plan.qk_bytes + plan.mbox_bytes) return GDN_EWORKSPACE;
+    if (workspace_bytes < plan.total_bytes) return GDN_EWORKSPACE;
 
     PrefillParams p;
     p.q = q; p.k = k; p.v = v; p.z = norm ? z : nullptr; p.conv_w = conv_w; p.norm_w = norm ? norm_w : nullptr;

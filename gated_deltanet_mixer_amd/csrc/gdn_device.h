@@ -18,6 +18,7 @@ namespace gdn {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16-byte copy unit kept in registers
 
 // ---------------------------------------------------------------- conversions
 
@@ -72,6 +73,18 @@ __device__ __forceinline__ float group_sum(float v) {
     for (int o = W / 2; o >= 1; o >>= 1)
         v += __shfl_xor(v, o, 64);
     return v;
+}
+
+// ---------------------------------------------------------------- barriers
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every
+// outstanding global load and store of the wave; kernels whose waves exchange
+// data through LDS alone use this instead, so prefetches and output stores
+// stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---------------------------------------------------------------- MFMA

@@ -25,12 +25,16 @@ struct PrefillParams {
     float eps_l2, eps_norm;
 };
 
-// Value-dimension slicing chosen for a prefill shape (columns per workgroup).
+// Value-dimension slicing and workspace layout chosen for a prefill shape.
 struct PrefillPlan {
-    int bv;          // 16, 32 or 64 value columns per workgroup
-    int nslice;      // 128 / bv
-    size_t qk_bytes;     // fp16 normalised q/k operands
+    int nt;              // 16-column value tiles per chain workgroup: 1 or 2
+    int bv;              // value columns per chain workgroup (16 * nt)
+    int nslice;          // workgroups per (sequence, value head): 128 / bv
+    int nchunks;         // ceil(T / 64)
+    size_t qk_bytes;     // per (sequence, chunk, key head): q^, k^ [64][128], k^T [128][64] fp16
+    size_t tp_bytes;     // per (sequence, chunk, value head): T diag(beta), P (lower blocks, fp16), decay vectors
     size_t mbox_bytes;   // exchange area (tagged partial sums, counters, error word)
+    size_t total_bytes;
 };
 
 int plan_prefill(int B, int T, int Hk, int Hv, PrefillPlan *plan);
