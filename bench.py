@@ -172,9 +172,11 @@ def bench_decode(torch, gdn, steps, warmup):
     return res
 
 
-def cpu_baseline(name, budget_s=20.0):
-    """The fp64 oracle (as it stands) on this host: the headline workload's
-    chains, as many as fit the time budget (at least one full chain)."""
+def cpu_baseline(name, budget_s=20.0, min_s=10.0):
+    """The fp64 oracle (as it stands) on this host's cores, on the headline
+    workload: all of its (sequence, value-head) chains, repeated until about
+    `min_s` seconds have passed, or as many whole chains as fit `budget_s` when
+    one full pass would take longer."""
     import numpy as np
     import gdn_inputs as GI
     from oracle import oracle as O
@@ -182,22 +184,56 @@ def cpu_baseline(name, budget_s=20.0):
     inp = GI.make_inputs(w)
     nchains = w.B * w.Hv
     threads = O.num_threads()
-    # calibrate on one chain, then take as many whole chains as fit the budget
+    # calibrate on one chain
     t = time.perf_counter()
     O.prefill(inp, w.B, w.T, w.Hk, w.Hv, w.conv, w.norm, chains=[0], threads=1, want_conv_state=False)
     one = time.perf_counter() - t
     per_round = max(1, min(threads, nchains))
-    n = int(min(nchains, max(per_round, per_round * (budget_s // max(one, 1e-9)))))
-    chains = np.arange(n) % nchains
+    full_est = one * math.ceil(nchains / per_round)
+    if full_est <= budget_s:
+        chains = np.arange(nchains)
+    else:
+        n = int(max(per_round, per_round * (budget_s // max(one, 1e-9))))
+        chains = np.arange(min(n, nchains))
+    reps, el = 0, 0.0
     t = time.perf_counter()
-    O.prefill(inp, w.B, w.T, w.Hk, w.Hv, w.conv, w.norm, chains=chains, threads=threads, want_conv_state=False)
-    el = time.perf_counter() - t
+    while reps == 0 or (el < min_s and reps < 200):
+        O.prefill(inp, w.B, w.T, w.Hk, w.Hv, w.conv, w.norm, chains=chains, threads=threads,
+                  want_conv_state=False)
+        reps += 1
+        el = time.perf_counter() - t
+    n = len(chains)
     used = min(threads, n)
     # tokens/s of the layer = chain-tokens/s divided by the layer's Hv chains per token
-    return {"value": n * w.T / el / w.Hv, "unit": "tokens/s", "cores": used, "kind": "oracle",
+    return {"value": reps * n * w.T / el / w.Hv, "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": f"{n} of {nchains} (sequence, value-head) chains of {name}, all {w.T} tokens each, "
-                      f"fp64 C oracle with OpenMP over chains; {el:.1f} s wall",
+                      f"{reps} pass(es); fp64 C oracle (conv, L2 norm, token-by-token recurrence, gated "
+                      f"RMSNorm) with OpenMP over chains; {el:.1f} s wall",
             "host_cpus": os.cpu_count()}
+
+
+TRAFFIC_FILES = {"qwen35_0p8b_prefill_T4096": "profiles/prefill_qwen35_0p8b_T4096_hbm_traffic.txt"}
+
+
+def measured_traffic(name):
+    """HBM bytes per call from the committed counter summary of this workload,
+    or None when there is none or the kernel sources changed since it was taken."""
+    import hashlib
+    rel = TRAFFIC_FILES.get(name)
+    if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
+        return None
+    rec = {}
+    for line in open(os.path.join(ROOT, rel)):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_call", "sources_sha256", "sources"):
+            k, v = line.split(":", 1)
+            rec[k] = v.strip()
+    if not all(k in rec for k in ("traffic_bytes_per_call", "sources_sha256", "sources")):
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"].split():
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return int(rec["traffic_bytes_per_call"]) if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def main(argv=None):
@@ -208,6 +244,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="qwen35_0p8b_prefill_T4096", choices=sorted(WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="skip decode and the other prefill shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy three times (calibrates HBM byte counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the mixer path here has no "
@@ -220,6 +258,14 @@ def main(argv=None):
         print("no GPU visible", file=sys.stderr)
         return 1
 
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     head = bench_prefill(torch, gdn, args.workload, args.steps, args.warmup)
     extra = {}
     if not args.no_extra:
@@ -246,9 +292,9 @@ def main(argv=None):
         "config": {"workload": args.workload, "B": B, "T": T, "Hk": Hk, "Hv": Hv, "Dk": D, "Dv": D,
                    "chunk": C, "conv_width": 4, "gated_norm": True, "parallelism": "single GPU"},
         "roofline": {
-            "kernel": "gdn_prefill call (qk_prep_kernel + chain_kernel)",
+            "kernel": "one gdn_prefill call = chunk_prep_kernel + chain_kernel launches, timed together",
             "bound": "hbm", "achieved": head["hbm_GBps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-            "frac": head["hbm_frac"], "traffic": None,
+            "frac": head["hbm_frac"], "traffic": measured_traffic(args.workload),
             "mfma_useful_TFLOPs": head["useful_TFLOPs"], "mfma_useful_frac": head["mfma_useful_frac"],
         },
         "detail": {"headline": head, **extra},

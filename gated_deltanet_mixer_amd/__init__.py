@@ -5,7 +5,7 @@ libgdn.so.  Tensors are torch tensors on the GPU (bf16 tensors may be
 torch.bfloat16 or 16-bit integer views of the same bits); ``None`` passes a
 NULL pointer.  Work is enqueued on torch's current stream unless ``stream`` is
 given.  A non-zero status raises GdnError.  The import fails loudly when
-libgdn.so has not been built (``python -m gated_deltanet_mixer_amd.build``).
+libgdn.so has not been built (``python gated_deltanet_mixer_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -25,7 +25,10 @@ GDN_NO_NORM = 1
 
 class GdnError(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn}: {gdn_status_string(status)} (status {status})")
+        msg = f"{fn}: {gdn_status_string(status)} (status {status})"
+        if status == GDN_EHIP:
+            msg += f": {gdn_last_error()}"
+        super().__init__(msg)
         self.status = status
 
 
@@ -40,20 +43,30 @@ def make_shape(B: int, T: int, Hk: int, Hv: int, conv: bool = True, norm: bool =
     return gdn_shape(B, T, Hk, Hv, Dk, Dv, 4 if conv else 0, 0 if norm else GDN_NO_NORM, eps_l2, eps_norm)
 
 
+# torch ships its own copy of the HIP runtime under the same soname.  Loading
+# torch first makes libgdn.so bind to that copy, so the process holds one HIP
+# runtime and the library sees the device and the streams torch created.
+try:
+    import torch  # noqa: F401
+except ImportError:  # host-only use (argument checks, symbol inspection)
+    pass
+
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gated_deltanet_mixer_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python gated_deltanet_mixer_amd/build.py`")
 _lib = C.CDLL(LIB_PATH)
 _vp = C.c_void_p
 _sp = C.POINTER(gdn_shape)
 _lib.gdn_status_string.argtypes = [C.c_int]
 _lib.gdn_status_string.restype = C.c_char_p
+_lib.gdn_last_error.argtypes = []
+_lib.gdn_last_error.restype = C.c_char_p
 _lib.gdn_state_init.argtypes = [_sp, _vp, _vp, _vp]
 _lib.gdn_prefill_workspace_size.argtypes = [_sp, C.POINTER(C.c_size_t)]
 _lib.gdn_prefill.argtypes = [_sp] + [_vp] * 14 + [C.c_size_t, _vp]
 _lib.gdn_decode_step.argtypes = [_sp] + [_vp] * 12
 
 EXPORTED = ("gdn_state_init", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
-            "gdn_status_string")
+            "gdn_status_string", "gdn_last_error")
 
 
 def _ptr(t):
@@ -78,6 +91,10 @@ def _check(fn: str, rc: int) -> None:
 
 def gdn_status_string(status: int) -> str:
     return _lib.gdn_status_string(status).decode()
+
+
+def gdn_last_error() -> str:
+    return _lib.gdn_last_error().decode()
 
 
 def gdn_state_init(shape: gdn_shape, state, conv_state=None, stream=None) -> None:

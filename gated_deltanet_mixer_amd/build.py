@@ -1,6 +1,6 @@
 """Build libgdn.so (the mixer's C ABI and its gfx950 HIP kernels) in place.
 
-    python -m gated_deltanet_mixer_amd.build
+    python gated_deltanet_mixer_amd/build.py
 """
 from __future__ import annotations
 

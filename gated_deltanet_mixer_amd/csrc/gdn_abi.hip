@@ -7,6 +7,7 @@
 
 #include "gdn.h"
 #include "gdn_internal.h"
+#include <stdio.h>
 
 namespace gdn {
 namespace {
@@ -175,16 +176,37 @@ int gdn_decode_step(const gdn_shape *s, const uint16_t *q, const uint16_t *k, co
 } // extern "C"
 
 namespace gdn {
+
+namespace {
+thread_local char g_last_error[256] = "";
+}
+
+int fail(const char *what, hipError_t e) {
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return -1;
+}
+
+int fail(const char *what) {
+    snprintf(g_last_error, sizeof g_last_error, "%s", what);
+    return -1;
+}
+
 int launch_state_init(float *state, size_t n_state, uint16_t *conv_state, size_t n_conv, hipStream_t stream) {
-    const size_t n16s = n_state * sizeof(float) / 16;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(256), 0, stream, reinterpret_cast<uint4 *>(state), n16s);
-    if (hipGetLastError() != hipSuccess) return -1;
+    uint4 *ps = reinterpret_cast<uint4 *>(state);
+    size_t n16s = n_state * sizeof(float) / 16;
+    void *args_s[] = {&ps, &n16s};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(fill_zero_kernel), dim3(1024), dim3(256), args_s, 0,
+                                   stream);
+    if (e != hipSuccess) return fail("hipLaunchKernel(fill_zero_kernel, state)", e);
     if (conv_state && n_conv) {
-        const size_t n16c = n_conv * sizeof(uint16_t) / 16;
-        hipLaunchKernelGGL(fill_zero_kernel, dim3(256), dim3(256), 0, stream, reinterpret_cast<uint4 *>(conv_state),
-                           n16c);
-        if (hipGetLastError() != hipSuccess) return -1;
+        uint4 *pc = reinterpret_cast<uint4 *>(conv_state);
+        size_t n16c = n_conv * sizeof(uint16_t) / 16;
+        void *args_c[] = {&pc, &n16c};
+        e = hipLaunchKernel(reinterpret_cast<const void *>(fill_zero_kernel), dim3(256), dim3(256), args_c, 0, stream);
+        if (e != hipSuccess) return fail("hipLaunchKernel(fill_zero_kernel, conv state)", e);
     }
     return 0;
 }
 } // namespace gdn
+
+extern "C" const char *gdn_last_error(void) { return gdn::g_last_error; }

@@ -221,10 +221,11 @@ int launch_decode(const DecodeParams &p, hipStream_t stream) {
     a.conv = p.conv_width == 4; a.norm = p.norm;
     a.eps_l2 = p.eps_l2; a.eps_norm = p.eps_norm;
     const size_t lds = sizeof(float) * ((size_t)2 * kD + (size_t)kD * a.r + 2 * kD + 8 * kD + kD + 8);
-    if (lds > 160 * 1024) return -1;
-    const dim3 grid((unsigned)(p.B * p.Hk)), block(kThreads);
-    hipLaunchKernelGGL(decode_kernel, grid, block, lds, stream, a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    if (lds > 160 * 1024) return fail("decode: head ratio needs more LDS than a workgroup has");
+    void *args[] = {&a};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(decode_kernel), dim3((unsigned)(p.B * p.Hk)),
+                                         dim3(kThreads), args, lds, stream);
+    return e == hipSuccess ? 0 : fail("hipLaunchKernel(decode_kernel)", e);
 }
 
 } // namespace gdn

@@ -87,6 +87,15 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---------------------------------------------------------------- hardware ids
+
+// Index of the XCD (accelerator complex die) the calling wave runs on.
+__device__ __forceinline__ unsigned int xcc_id() {
+    unsigned int v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
+    return v;
+}
+
 // ---------------------------------------------------------------- MFMA
 
 __device__ __forceinline__ floatx4 mfma16x16x32(const half8 &a, const half8 &b, const floatx4 &c) {

@@ -37,6 +37,11 @@ struct PrefillPlan {
     size_t total_bytes;
 };
 
+// Record why a launch failed, for gdn_last_error() on the calling thread;
+// both return -1 so a launcher can `return fail(...)`.
+int fail(const char *what, hipError_t e);
+int fail(const char *what);
+
 int plan_prefill(int B, int T, int Hk, int Hv, PrefillPlan *plan);
 int launch_decode(const DecodeParams &p, hipStream_t stream);
 int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream);

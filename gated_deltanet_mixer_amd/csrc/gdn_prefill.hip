@@ -39,9 +39,11 @@
 //                     chunk c runs.  The norm needs all 128 columns of a row:
 //                     every 16-column tile publishes per-row sums of squares
 //                     as tagged 64-bit words (value | chunk tag) and the
-//                     helpers read all eight one chunk later.  Sibling slices
-//                     are co-resident (cooperative launch), every wait is
-//                     bounded.
+//                     helpers read all of them two chunks later.  Slices are
+//                     handed out from per-XCD ticket queues in the order
+//                     workgroups start, so a slice only ever waits for
+//                     siblings that are running or next in line; every wait
+//                     is bounded.
 // All contractions use fp16 MFMA operands with fp32 accumulation; the state is
 // carried in fp32 across chunks; inputs and outputs are bf16.
 #include "gdn_device.h"
@@ -382,6 +384,8 @@ struct ChainArgs {
     unsigned long long *mbox;  // [B*Hv][kTiles][kRing][64]: per-row sums of squares of each slice
     unsigned int *counters;    // [B*Hv]
     unsigned int *err;
+    unsigned int *tickets;     // [8] next item of each XCD queue
+    unsigned int *exits;       // workgroups that have left the item loop
     int B, T, Hk, Hv, r, Cc, conv, norm, nch, n_items, grid;
     float eps_norm;
 };
@@ -680,11 +684,39 @@ __global__ __launch_bounds__(256) void chain_kernel(ChainArgs a) {
     const int htid = tid - NT * 64;                       // helper index
     const int hcg = (htid >= 0 ? htid : 0) % NCG;         // fixed column group of a helper (NH % NCG == 0)
 
-    const int p = blockIdx.x;
-    const int slot = (a.grid % 8 == 0) ? (p % 8) * (a.grid / 8) + p / 8 : p;
     int broken = 0;
+    __shared__ int s_item;
+    // Work items (chain, slice) come from eight queues, one per XCD: chain c
+    // sits in queue c % 8 and its slices are consecutive tickets.  A workgroup
+    // serves the queue of the XCD it runs on (the slices of a chain then share
+    // that XCD's L2), and the other queues once its own is empty.  Tickets are
+    // taken only when a workgroup starts an item, so the items begun form a
+    // prefix of every queue: the slices a workgroup waits for are either
+    // running or next in line for the next free workgroup, and no launch-wide
+    // co-residency is needed.
+    const int xcc = static_cast<int>(xcc_id() & 7u);
+    const int n_chains = a.B * a.Hv;
+    int qi = 0;
 
-    for (int item = slot; item < a.n_items; item += a.grid) {
+    for (;;) {
+        if (tid == 0) {
+            int item = -1;
+            for (; qi < 8 && item < 0; ) {
+                const int q = (xcc + qi) & 7;
+                const int nq = n_chains > q ? (n_chains - q + 7) / 8 : 0;
+                const unsigned int t = __hip_atomic_fetch_add(a.tickets + q, 1u, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT);
+                if (t < (unsigned int)(nq * NSL))
+                    item = (q + 8 * (int)(t / NSL)) * NSL + (int)(t % NSL);
+                else
+                    ++qi;
+            }
+            s_item = item;
+        }
+        __syncthreads();
+        const int item = s_item;
+        __syncthreads();
+        if (item < 0) break;
         const int chain = item / NSL, s = item % NSL;
         const int b = chain / a.Hv, h = chain % a.Hv, kh = h / a.r;
         const int sv0 = s * BV;
@@ -883,6 +915,15 @@ __global__ __launch_bounds__(256) void chain_kernel(ChainArgs a) {
         }
         lds_barrier();
     }
+    // the last workgroup out rewinds the queues for the next launch
+    if (tid == 0) {
+        const unsigned int done =
+            __hip_atomic_fetch_add(a.exits, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (unsigned int)a.grid - 1) {
+            for (int q = 0; q < 8; ++q) __hip_atomic_store(a.tickets + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -892,27 +933,28 @@ int launch_chain(const ChainArgs &base, hipStream_t stream) {
     ChainArgs a = base;
     constexpr size_t lds = ChainLds<NT>::bytes;
     auto fn = chain_kernel<NT>;
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
-        return -1;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return fail("hipFuncSetAttribute(chain_kernel)", e);
     int dev = 0, ncu = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn), 256, lds) !=
-            hipSuccess ||
-        per_cu < 1)
-        return -1;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return fail("hipGetDevice", e);
+    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return fail("hipDeviceGetAttribute(multiprocessor count)", e);
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn), 256, lds)) !=
+        hipSuccess)
+        return fail("hipOccupancyMaxActiveBlocksPerMultiprocessor(chain_kernel)", e);
     constexpr int NSL = kTiles / NT;
+    // One workgroup per resident slot at most: a workgroup that waits for its
+    // sibling slices holds its slot, and the ticket order lets the next free
+    // slot start them.  At least 8 * NSL slots keep a started slice of every
+    // queue from blocking all slots.
     const int cap = ncu * per_cu;
-    const int unit = 8 * NSL;  // keeps sibling slices contiguous inside one XCD's share
-    int grid = a.n_items <= cap ? ((a.n_items + unit - 1) / unit) * unit : (cap / unit) * unit;
-    if (grid > cap) grid = (cap / unit) * unit;
-    if (grid < NSL) return -1;
+    if (cap < 8 * NSL) return fail("chain_kernel: fewer resident workgroup slots than eight heads' slices");
+    const int grid = a.n_items < cap ? a.n_items : cap;
     a.grid = grid;
     void *args[] = {&a};
-    const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(fn), dim3(grid), dim3(256),
-                                                    args, (unsigned)lds, stream);
-    return e == hipSuccess ? 0 : -1;
+    e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(grid), dim3(256), args, lds, stream);
+    return e == hipSuccess ? 0 : fail("hipLaunchKernel(chain_kernel)", e);
 }
 
 } // namespace
@@ -940,6 +982,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     const size_t chains = (size_t)p.B * p.Hv;
     const size_t mbox_sz = align256(chains * kTiles * kRing * kC * sizeof(unsigned long long));
     unsigned int *counters = reinterpret_cast<unsigned int *>(mb + mbox_sz);
+    // last 256 bytes: error word, then the eight queue tickets and the exit count
     unsigned int *err = reinterpret_cast<unsigned int *>(mb + mbox_sz + align256(chains * sizeof(unsigned int)));
 
     PrepArgs pa;
@@ -949,25 +992,28 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     pa.B = p.B; pa.T = p.T; pa.Hk = p.Hk; pa.Hv = p.Hv; pa.r = p.Hv / p.Hk;
     pa.Cc = 2 * p.Hk * kD + p.Hv * kD; pa.conv = p.conv_width == 4; pa.nch = plan.nchunks;
     pa.eps_l2 = p.eps_l2;
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)PrepLds::bytes) != hipSuccess)
-        return -1;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)plan.nchunks, (unsigned)p.Hk, (unsigned)p.B), dim3(256),
-                       PrepLds::bytes, stream, pa);
-    if (hipGetLastError() != hipSuccess) return -1;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)PrepLds::bytes);
+    if (e != hipSuccess) return fail("hipFuncSetAttribute(chunk_prep_kernel)", e);
+    void *pargs[] = {&pa};
+    e = hipLaunchKernel(reinterpret_cast<const void *>(chunk_prep_kernel),
+                        dim3((unsigned)plan.nchunks, (unsigned)p.Hk, (unsigned)p.B), dim3(256), pargs, PrepLds::bytes,
+                        stream);
+    if (e != hipSuccess) return fail("hipLaunchKernel(chunk_prep_kernel)", e);
 
     ChainArgs a;
     a.qkw = qkw; a.tpw = tpw;
     a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w; a.conv_state_in = p.conv_state_in;
     a.state_in = p.state_in; a.o = p.o; a.conv_state_out = p.conv_state_out; a.state_out = p.state_out;
     a.mbox = reinterpret_cast<unsigned long long *>(mb); a.counters = counters; a.err = err;
+    a.tickets = err + 16; a.exits = err + 32;
     a.B = p.B; a.T = p.T; a.Hk = p.Hk; a.Hv = p.Hv; a.r = pa.r; a.Cc = pa.Cc; a.conv = pa.conv; a.norm = p.norm;
     a.nch = plan.nchunks; a.n_items = (int)(chains * plan.nslice); a.grid = 0;
     a.eps_norm = p.eps_norm;
     switch (plan.nt) {
     case 1: return launch_chain<1>(a, stream);
     case 2: return launch_chain<2>(a, stream);
-    default: return -1;
+    default: return fail("prefill plan: unsupported value-tile count");
     }
 }
 

@@ -79,9 +79,13 @@ int gdn_state_init(const gdn_shape *shape, float *state, uint16_t *conv_state, v
 
 /*
  * Bytes of device workspace gdn_prefill needs for `shape` (written to *bytes).
- * The workspace holds the normalised q/k operands (fp16, B*T*Hk*2*Dk values)
- * and the per-row sums of squares that workgroups sharing one head exchange
- * for the gated RMSNorm.
+ * The workspace holds the state-independent chunk operands that one kernel
+ * computes for the sequential pass of another: the normalised q/k rows (fp16,
+ * B*T*Hk*2*Dk values), per (chunk, value head) the packed lower-triangular
+ * T diag(beta) and (Q K^T) o R blocks and the decay vectors ("How Qwen3.5
+ * works" §9.11), and an exchange area: the per-row sums of squares that the
+ * workgroups sharing one head trade for the gated RMSNorm, work-queue tickets
+ * and an error word.  Returns GDN_EINVAL for a shape gdn_prefill would reject.
  */
 int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
 
@@ -137,6 +141,14 @@ int gdn_decode_step(const gdn_shape *shape, const uint16_t *q, const uint16_t *k
 
 /* A static, NUL-terminated description of a status code. */
 const char *gdn_status_string(int status);
+
+/*
+ * After a call on this thread returned GDN_EHIP: which HIP call or check
+ * failed and HIP's own message for it.  The string is owned by the library,
+ * stays valid until the thread's next failing call, and is empty before the
+ * first failure.
+ */
+const char *gdn_last_error(void);
 
 #ifdef __cplusplus
 }

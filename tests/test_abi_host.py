@@ -24,7 +24,12 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["gdn_decode_step", "gdn_prefill", "gdn_prefill_workspace_size", "gdn_state_init", "gdn_status_string"])
+        ["gdn_decode_step", "gdn_last_error", "gdn_prefill", "gdn_prefill_workspace_size", "gdn_state_init",
+         "gdn_status_string"])
+
+
+def test_last_error_is_a_string_before_any_failure():
+    assert isinstance(gdn.gdn_last_error(), str)
 
 
 def test_library_exports_every_declared_symbol():
@@ -157,3 +162,13 @@ def test_state_init_rejects_bad_arguments():
     assert f(C.byref(s), FAKE + 4, None, None) == gdn.GDN_EINVAL
     s0 = _shape(conv=False)
     assert f(C.byref(s0), FAKE, FAKE + MB * 512, None) == gdn.GDN_EINVAL
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding first must not load a second HIP runtime next to
+    torch's (two runtimes each claim the device; the second sees none)."""
+    code = ("import gated_deltanet_mixer_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT, check=True).stdout
+    assert out.strip() == "1"

@@ -1,0 +1,150 @@
+"""GPU checks of the call boundaries, through the C ABI, against the fp64 oracle.
+
+- A prefill split in two calls (state and conv state handed over) equals one
+  prefill over the whole sequence.
+- Prefill followed by decode steps equals one prefill over all tokens.
+- A workspace reused after a call on different inputs gives the result of a
+  fresh workspace, bit for bit (the exchange area is left clean).
+- Repeated calls are deterministic; state_out may alias state_in.
+- gdn_state_init zeroes the state and the conv state.
+"""
+import numpy as np
+import pytest
+
+import gdn_inputs as GI
+from oracle import oracle as O
+from tests.metrics import OUT_TOL, STATE_TOL, bf16_to_f64, out_errors, state_error
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+D = 128
+
+
+def _R():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gdn_run
+    return gdn_run
+
+
+def _slice_T(inp, t0, t1):
+    out = dict(inp)
+    for k in ("q", "k", "v", "z", "g", "beta"):
+        if inp.get(k) is not None:
+            out[k] = np.ascontiguousarray(inp[k][:, t0:t1])
+    return out
+
+
+def _y(R, o, B, Hv):
+    o = R.bits(o)
+    T = o.shape[1]
+    return np.stack([bf16_to_f64(o[c // Hv, :, c % Hv]) for c in range(B * Hv)]).reshape(B * Hv, T, D)
+
+
+def _check(name, y, y_ref, S, S_ref):
+    eo, es = out_errors(y, y_ref), state_error(S, S_ref)
+    print(f"[seam] {name}: e_out={eo['e_out']:.3e} e_state={es:.3e}", flush=True)
+    assert eo["nonfinite"] == 0
+    assert eo["e_out"] <= OUT_TOL
+    assert es <= STATE_TOL
+
+
+@pytest.mark.parametrize("T1,T2", [(100, 77), (64, 64), (2, 130), (130, 1)])
+def test_split_prefill_equals_whole(T1, T2):
+    R = _R()
+    B, Hk, Hv = 2, 2, 4
+    w = GI.Workload(f"split_{T1}_{T2}", B, T1 + T2, Hk, Hv, random_state=True, random_conv_state=True,
+                    tag=500 + T1 * 7 + T2)
+    inp = GI.make_inputs(w)
+    a = R.Prefill(_slice_T(inp, 0, T1), B, T1, Hk, Hv, True, True)
+    a.run()
+    b = R.Prefill(_slice_T(inp, T1, T1 + T2), B, T2, Hk, Hv, True, True,
+                  state_in=a.state_out, conv_state_in=a.conv_state_out)
+    b.run()
+    torch.cuda.synchronize()
+    assert a.exchange_error_word() == 0 and b.exchange_error_word() == 0
+    y_ref, S_ref, cs_ref = O.prefill(inp, B, T1 + T2, Hk, Hv, True, True)
+    y = np.concatenate([_y(R, a.o, B, Hv), _y(R, b.o, B, Hv)], axis=1)
+    S = b.state_out.cpu().numpy().reshape(-1, D, D)
+    _check(f"split {T1}+{T2}", y, y_ref, S, S_ref)
+    np.testing.assert_array_equal(R.bits(b.conv_state_out), cs_ref)
+
+
+def test_prefill_then_decode_steps():
+    R = _R()
+    B, Hk, Hv, T, steps = 3, 2, 6, 130, 3
+    w = GI.Workload("pre_dec", B, T + steps, Hk, Hv, random_state=True, random_conv_state=True, tag=600)
+    inp = GI.make_inputs(w)
+    pre = R.Prefill(_slice_T(inp, 0, T), B, T, Hk, Hv, True, True)
+    pre.run()
+    ys = [_y(R, pre.o, B, Hv)]
+    state = pre.state_out.clone()
+    conv_state = pre.conv_state_out.clone()
+    import gated_deltanet_mixer_amd as gdn
+    shape = gdn.make_shape(B, 1, Hk, Hv)
+    o = torch.empty((B, Hv, D), dtype=torch.int16, device="cuda")
+    for t in range(T, T + steps):
+        d = {k: R.to_dev(np.ascontiguousarray(inp[k][:, t])) for k in ("q", "k", "v", "z", "g", "beta")}
+        gdn.gdn_decode_step(shape, d["q"], d["k"], d["v"], d["g"], d["beta"], d["z"], pre.d["conv_w"],
+                            pre.d["norm_w"], state, conv_state, o)
+        ys.append(bf16_to_f64(R.bits(o)).reshape(B * Hv, 1, D))
+    torch.cuda.synchronize()
+    y_ref, S_ref, cs_ref = O.prefill(inp, B, T + steps, Hk, Hv, True, True)
+    _check("prefill+decode", np.concatenate(ys, axis=1), y_ref, state.cpu().numpy().reshape(-1, D, D), S_ref)
+    np.testing.assert_array_equal(R.bits(conv_state), cs_ref)
+
+
+def test_workspace_reuse_matches_fresh_workspace():
+    R = _R()
+    B, T, Hk, Hv = 1, 300, 2, 4
+    wa = GI.Workload("ws_a", B, T, Hk, Hv, random_state=True, tag=700)
+    wb = GI.Workload("ws_b", B, T, Hk, Hv, random_state=True, tag=701)
+    a = R.Prefill(GI.make_inputs(wa), B, T, Hk, Hv, True, True)
+    b = R.Prefill(GI.make_inputs(wb), B, T, Hk, Hv, True, True)
+    fresh = R.Prefill(GI.make_inputs(wb), B, T, Hk, Hv, True, True)
+    b.ws = a.ws  # b runs on the workspace a has just used
+    a.run()
+    b.run()
+    fresh.run()
+    torch.cuda.synchronize()
+    assert a.exchange_error_word() == 0 and b.exchange_error_word() == 0
+    assert torch.equal(b.o, fresh.o)
+    assert torch.equal(b.state_out, fresh.state_out)
+    assert torch.equal(b.conv_state_out, fresh.conv_state_out)
+
+
+def test_repeat_is_deterministic_and_state_may_alias():
+    R = _R()
+    B, T, Hk, Hv = 2, 257, 1, 3
+    w = GI.Workload("det", B, T, Hk, Hv, random_state=True, random_conv_state=True, tag=702)
+    inp = GI.make_inputs(w)
+    r = R.Prefill(inp, B, T, Hk, Hv, True, True)
+    r.run()
+    o1, s1 = r.o.clone(), r.state_out.clone()
+    r.run()
+    torch.cuda.synchronize()
+    assert torch.equal(r.o, o1) and torch.equal(r.state_out, s1)
+    # state_out aliasing state_in: the result is the same as with separate buffers
+    r.d["state_in"] = r.d["state_in"].clone()
+    r.state_out = r.d["state_in"]
+    r.run()
+    torch.cuda.synchronize()
+    assert torch.equal(r.o, o1) and torch.equal(r.state_out, s1)
+
+
+def test_state_init_zeroes():
+    _R()
+    import gated_deltanet_mixer_amd as gdn
+    B, Hk, Hv = 3, 2, 6
+    shape = gdn.make_shape(B, 1, Hk, Hv)
+    Cc = 2 * Hk * D + Hv * D
+    st = torch.full((B, Hv, D, D), 7.0, device="cuda")
+    cs = torch.full((B, 3, Cc), 123, dtype=torch.int16, device="cuda")
+    gdn.gdn_state_init(shape, st, cs)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(st)) == 0 and int(torch.count_nonzero(cs)) == 0
+    st.fill_(3.0)
+    gdn.gdn_state_init(shape, st, None)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(st)) == 0
