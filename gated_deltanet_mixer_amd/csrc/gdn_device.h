@@ -53,8 +53,13 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&f)[8]) {
 
 // ---------------------------------------------------------------- math
 
-// x * sigmoid(x), fp32 (expf: the correctly rounded-to-within-ulps libm form)
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// x * sigmoid(x) in fp32 from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp each).  Saturates correctly: a large
+// negative x gives exp2 -> inf, rcp -> 0.
+__device__ __forceinline__ float silu(float x) {
+    const float t = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+    return x * __builtin_amdgcn_rcpf(1.0f + t);
+}
 
 // ---------------------------------------------------------------- reductions
 

@@ -19,29 +19,34 @@
 //                     once per key head; then for each of its r value heads
 //                     the decays, T = (I + L)^{-1} (16x16 diagonal blocks by
 //                     substitution in fp32, the rest as block products on
-//                     MFMA), T diag(beta) and P = (Q K^T) o R as packed lower
-//                     16x16 blocks.  Everything that does not depend on the
-//                     state is done here, once, instead of inside the
-//                     sequential loop of every value slice.
-//  chain_kernel<NT>   one workgroup (4 waves, one per SIMD) per (sequence, value head,
-//                     slice of 16*NT value columns); state columns evolve
-//                     independently, so a head splits into 8/NT slices on
-//                     different CUs.  Waves 0..NT-1 each own one 16-column
+//                     MFMA), T diag(beta) and P = (Q K^T) o R.  Everything
+//                     that does not depend on the state is done here, once,
+//                     instead of inside the sequential loop of every value
+//                     slice.  Its outputs are written as MFMA operand
+//                     fragments (64 lanes x 16 bytes each), so the sequential
+//                     pass loads every operand straight into registers with
+//                     one coalesced 1 KB load per fragment.
+//  chain_kernel<NT>   one workgroup (4 waves, one per SIMD) per (sequence,
+//                     value head, slice of 16*NT value columns); state columns
+//                     evolve independently, so a head splits into 8/NT slices
+//                     on different CUs.  Waves 0..NT-1 each own one 16-column
 //                     tile of the state in MFMA accumulator registers and run
-//                     the chunk loop -- the only sequential dependency -- with
-//                     no LDS round trip or barrier inside a chunk: the
+//                     the chunk loop -- the only sequential dependency.  The
 //                     accumulator layout of two adjacent 16-row tiles is the
 //                     B-operand layout of a 16x16x32 MFMA under one fixed
-//                     permutation of k, applied to the A operand as well.  The
-//                     other waves convert v (conv + SiLU) for the next chunk
-//                     and apply the gated RMSNorm to the previous chunk.
-//                     Operands of chunk c+1 are fetched into registers while
-//                     chunk c runs.  The norm needs all 128 columns of a row:
+//                     permutation of k, applied to the A operands as well, so
+//                     no shuffle sits in the loop.  Each fragment register set
+//                     is reloaded with the next chunk's data right after its
+//                     last use, a full chunk ahead of its next use.  The other
+//                     waves load raw v and z, convert v (conv + SiLU) for the
+//                     next chunk, and finish the gated RMSNorm of an earlier
+//                     chunk; one LDS barrier per chunk hands tiles between
+//                     the roles.  The norm needs all 128 columns of a row:
 //                     every 16-column tile publishes per-row sums of squares
-//                     as tagged 64-bit words (value | chunk tag) and the
-//                     helpers read all of them two chunks later.  Slices are
-//                     handed out from per-XCD ticket queues in the order
-//                     workgroups start, so a slice only ever waits for
+//                     as tagged 64-bit words (value | chunk tag) and each
+//                     slice reads its siblings' words kLag chunks later.
+//                     Slices are handed out from per-XCD ticket queues in the
+//                     order workgroups start, so a slice only ever waits for
 //                     siblings that are running or next in line; every wait
 //                     is bounded.
 // All contractions use fp16 MFMA operands with fp32 accumulation; the state is
@@ -55,13 +60,17 @@ namespace {
 
 constexpr int kD = 128;        // head width
 constexpr int kC = 64;         // chunk length
-// Chunks of partial sums kept per tile.  A slice reads chunk c-3 in iteration
-// c, and a sibling cannot finish iteration c+2 before this slice has published
-// chunk c-1, so the newest chunk a sibling can be writing meanwhile is c+1: five
-// chunks live at once, eight slots keep the index a power of two.
+// The gated norm of chunk c-kLag is finished in iteration c (and applied in
+// c+1), so a slice reads its siblings' sums kLag-1 iterations after they were
+// published.  A sibling cannot finish iteration c+kLag-1 before this slice
+// has published chunk c-1, so chunks c-kLag .. c+kLag-1 may be live in the
+// mailbox at once: kRing >= 2 kLag slots.
+constexpr int kLag = 4;
 constexpr int kRing = 8;
+constexpr int kORing = 8;      // pre-norm output tiles kept in LDS (>= kLag + 2)
 constexpr int kTiles = 8;      // 16-column tiles per head
 constexpr uint32_t kSpinLimit = 1u << 20;  // bound of every cross-workgroup wait (~0.3 s)
+static_assert(kRing >= 2 * kLag && kORing >= kLag + 2, "pipeline depth");
 
 // LDS pitches (elements) so that 16-row MFMA fragment reads hit distinct banks.
 constexpr int P128 = kD + 8;   // fp16 rows of 128
@@ -69,18 +78,24 @@ constexpr int P64 = kC + 8;    // fp16 rows of 64
 constexpr int PL = kC + 4;     // fp32 rows of 64
 constexpr int PTD = 20;        // fp32 rows of a 16x16 block
 
-// Workspace blocks (in fp16 elements).  Matrices that the chain kernel reads
-// as MFMA A operands are stored with their contraction index permuted inside
-// every 32-wide block, so that each lane's eight k-values (original indices
-// 4q..4q+3 and 16+4q..16+4q+3, matching the accumulator layout of two
-// adjacent 16-row tiles) are contiguous: stored position p holds original
-// index 4*(p>>3) + (p&3) + 16*((p>>2)&1).  kpos(m) is where the original
-// 4-group m (indices 4m..4m+3) of a 32-block starts.
+// Workspace blocks (fp16 elements), written by the prep kernel as MFMA operand
+// fragments: fragment f holds, for lane L = l16 + 16 lq, the 8 values of row
+// (tile row) + l16 at contraction indices 32 ks + {4 lq .. 4 lq + 3} and
+// 32 ks + 16 + {4 lq .. 4 lq + 3} -- the rows of two adjacent 16-row
+// accumulator tiles as they sit in one lane, i.e. the contraction index of
+// each 32-block taken in the order 4*(p>>3) + (p&3) + 16*((p>>2)&1).
+//   per (sequence, chunk, key head), kQKF:  q^ f = 0..15 (row tile f>>2, k-step f&3 over keys),
+//                                           k^ f = 16..31 (same), k^T f = 32..47 (key-row tile
+//                                           (f-32)>>1, k-step (f-32)&1 over tokens)
+//   per (sequence, chunk, value head), kTPF: T diag(beta) f = 0..5, P = (Q K^T) o R f = 6..11
+//                                           (lower-triangular 64x64, only the blocks that are
+//                                           not all zero), then fp32 e^{G_i} [64],
+//                                           e^{G_C - G_i} [64], e^{G_C} [4]
 constexpr int kBlk = 256;                              // one 16x16 block (prep staging)
-constexpr int kQK = 2 * kC * kD;                       // q^ [64][128], k^ [64][128] (keys permuted)
-constexpr int kTri = 32 * 32 + 32 * 64;                // lower triangle at 32-granularity: rows 0-31 x 32, rows 32-63 x 64
-constexpr int kTP = 2 * kTri + 2 * 2 * kC;             // T diag(beta), P (tokens permuted), then 2 x 64 fp32
-constexpr int kTPVec = 2 * kTri;                       // offset of the fp32 decay vectors
+constexpr int kFrag = 64 * 8;                          // one fragment: 64 lanes x 8 fp16
+constexpr int kQKF = 48 * kFrag;
+constexpr int kVecOff = 12 * kFrag;
+constexpr int kTPF = kVecOff + 2 * 256;                // + 256 fp32
 
 __host__ __device__ constexpr int kpos(int m) { return m < 4 ? 8 * m : 8 * (m - 4) + 4; }
 
@@ -109,8 +124,8 @@ struct PrepArgs {
     const uint16_t *q, *k, *conv_w, *conv_state_in;
     const float *g, *beta;
     uint16_t *conv_state_out;
-    _Float16 *qkw;  // [B][nch][Hk][kQK]
-    _Float16 *tpw;  // [B][nch][Hv][kTP]
+    _Float16 *qkf;  // [B][nch][Hk][kQKF]
+    _Float16 *tpf;  // [B][nch][Hv][kTPF]
     int B, T, Hk, Hv, r, Cc, conv, nch;
     float eps_l2;
 };
@@ -145,7 +160,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     const int l16 = lane & 15, lq = lane >> 4;
     const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
     const int tc0 = c * kC;
-    _Float16 *qkb = a.qkw + (((size_t)b * a.nch + c) * a.Hk + kh) * kQK;
 
     // ---- 1. q/k rows: conv + SiLU + L2 norm.  Thread = (4-token segment, q|k, 8 channels)
     {
@@ -199,10 +213,6 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
                 }
                 const int row = tl0 + i;
                 *reinterpret_cast<half8 *>((m ? sK : sQ) + row * P128 + cg * 8) = hv;
-                _Float16 *gdst = qkb + m * kC * kD + row * kD + 32 * (cg >> 2);
-                const int g2 = 2 * (cg & 3);  // original 4-groups g2, g2+1 of this 32-block
-                *reinterpret_cast<half4 *>(gdst + kpos(g2)) = half4{hv[0], hv[1], hv[2], hv[3]};
-                *reinterpret_cast<half4 *>(gdst + kpos(g2 + 1)) = half4{hv[4], hv[5], hv[6], hv[7]};
             }
         }
         // raw q/k inputs of the last three tokens -> conv state out
@@ -219,6 +229,31 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
         }
     }
     lds_barrier();
+
+    // ---- 1b. q^, k^ and k^T to the workspace as operand fragments
+    {
+        _Float16 *qkb = a.qkf + (((size_t)b * a.nch + c) * a.Hk + kh) * kQKF;
+        for (int idx = tid; idx < 48 * 64; idx += 256) {
+            const int f = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
+            half8 v;
+            if (f < 32) {
+                const _Float16 *M = f < 16 ? sQ : sK;
+                const int ff = f & 15;
+                const _Float16 *src = M + (16 * (ff >> 2) + fl) * P128 + 32 * (ff & 3) + 4 * fq;
+                const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
+                v = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                const int ff = f - 32;
+                const int key = 16 * (ff >> 1) + fl, tok = 32 * (ff & 1) + 4 * fq;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[j] = sK[(tok + j) * P128 + key];
+                    v[4 + j] = sK[(tok + 16 + j) * P128 + key];
+                }
+            }
+            *reinterpret_cast<half8 *>(qkb + (size_t)idx * 8) = v;
+        }
+    }
 
     // ---- 2. raw K K^T and Q K^T lower tiles, kept in registers (5 tasks per wave)
     floatx4 raw[5];
@@ -244,7 +279,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     // ---- 3. per value head of this key head
     for (int hr = 0; hr < a.r; ++hr) {
         const int h = kh * a.r + hr;
-        _Float16 *tpb = a.tpw + (((size_t)b * a.nch + c) * a.Hv + h) * kTP;
+        _Float16 *tpb = a.tpf + (((size_t)b * a.nch + c) * a.Hv + h) * kTPF;
         if (wave == 0) {
             const int t = tc0 + lane;
             const bool valid = t < a.T;
@@ -259,9 +294,10 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
             const float gc = __shfl(gv, 63, 64);
             sG[lane] = gv;
             sB[lane] = bv;
-            float *vec = reinterpret_cast<float *>(tpb + kTPVec);
+            float *vec = reinterpret_cast<float *>(tpb + kVecOff);
             vec[lane] = __expf(gv);
             vec[kC + lane] = __expf(gc - gv);
+            if (lane < 4) vec[2 * kC + lane] = __expf(gc);
         }
         lds_barrier();
 
@@ -346,26 +382,34 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
         }
         lds_barrier();
 
-        // T diag(beta) and P to the workspace: lower triangle at 32-granularity, tokens
-        // (columns) permuted inside 32-blocks; 8-byte groups of 4 columns
-        for (int idx = tid; idx < 2 * kTri / 4; idx += 256) {
-            const int mat = idx >= kTri / 4, j = mat ? idx - kTri / 4 : idx;
-            int r, cb, m, dst;
-            if (j < 256) {
-                r = j >> 3, cb = 0, m = j & 7;
-                dst = r * 32 + kpos(m);
-            } else {
-                const int j2 = j - 256;
-                r = 32 + (j2 >> 4), cb = (j2 >> 3) & 1, m = j2 & 7;
-                dst = 32 * 32 + (r - 32) * 64 + 32 * cb + kpos(m);
+        // T diag(beta) (fragments 0..5) and P (6..11) to the workspace
+        for (int idx = tid; idx < 12 * 64; idx += 256) {
+            const int f = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
+            const int g = f < 6 ? f : f - 6;
+            int row, ks;
+            if (g < 2) {
+                row = 16 * g + fl;
+                ks = 0;
+            } else if (f < 6) {  // T diag(beta): rows 32..63 take both k-steps
+                row = 32 + 16 * ((g - 2) >> 1) + fl;
+                ks = (g - 2) & 1;
+            } else {              // P: row tiles 2, 3 take both k-steps
+                row = 16 * (2 + ((g - 2) >> 1)) + fl;
+                ks = (g - 2) & 1;
             }
-            const int oc = 32 * cb + 4 * m;  // first original column of the group
-            half4 v4 = {0, 0, 0, 0};
-            if ((oc >> 4) <= (r >> 4)) {
-                const int blk = (r >> 4) * ((r >> 4) + 1) / 2 + (oc >> 4);
-                v4 = *reinterpret_cast<const half4 *>((mat ? sPst : sTbst) + blk * kBlk + (r & 15) * 16 + (oc & 15));
+            const _Float16 *stg = f < 6 ? sTbst : sPst;
+            const int bi = row >> 4;
+            half8 v;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int col = 32 * ks + 16 * hh + 4 * fq;  // 4 columns inside one 16-block
+                const int bj = col >> 4;
+                half4 q4 = {0, 0, 0, 0};
+                if (bj <= bi) q4 = lds_half4(stg + (bi * (bi + 1) / 2 + bj) * kBlk + (row & 15) * 16 + (col & 15));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }
-            *reinterpret_cast<half4 *>(tpb + mat * kTri + dst) = v4;
+            *reinterpret_cast<half8 *>(tpb + (size_t)idx * 8) = v;
         }
         lds_barrier();
     }
@@ -376,7 +420,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 // ========================================================================
 
 struct ChainArgs {
-    const _Float16 *qkw, *tpw;
+    const _Float16 *qkf, *tpf;
     const uint16_t *v, *z, *conv_w, *norm_w, *conv_state_in;
     const float *state_in;
     uint16_t *o, *conv_state_out;
@@ -393,137 +437,168 @@ struct ChainArgs {
 template <int NT>
 struct ChainLds {
     static constexpr int BV = 16 * NT;
-    static constexpr int PV = BV + 4;
-    static constexpr size_t sQ = 0;                          // fp16 [64][P128]   q^
-    static constexpr size_t sK = sQ + 2 * kC * P128;         // fp16 [64][P128]   k^
-    static constexpr size_t sKT = sK + 2 * kC * P128;        // fp16 [128][P64]   k^T
-    static constexpr size_t sTb = sKT + 2 * kD * P64;        // fp16 [64][P64]    T diag(beta)
-    static constexpr size_t sP = sTb + 2 * kC * P64;         // fp16 [64][P64]    (Q K^T) o R
-    static constexpr size_t sEG = sP + 2 * kC * P64;         // fp32 [64] e^G, then [64] e^{G_C - G}
-    static constexpr size_t sV = sEG + 4 * 2 * kC;           // fp32 [2][64][PV]  conv(v) of the slice
-    static constexpr size_t sO = sV + 4 * 2 * kC * PV;       // fp32 [5][64][PV]  pre-norm output
-    static constexpr size_t sRawV = sO + 4 * 5 * kC * PV;    // bf16 [2][64][BV]  raw v of the slice
-    static constexpr size_t sZ = sRawV + 2 * 2 * kC * BV;    // bf16 [64][BV]     z of the slice
-    static constexpr size_t sRstd = sZ + 2 * kC * BV;        // fp32 [2][64]      gated-norm 1/rms per row
-    static constexpr size_t sCW = sRstd + 4 * 2 * kC;        // fp32 [BV][4]      conv taps of the slice's v channels
-    static constexpr size_t sNW = sCW + 4 * 4 * BV;          // fp32 [BV]         gated-norm weights of the slice
+    static constexpr int VT = BV * PL;                       // floats of one column-major [BV][64] tile
+    static constexpr size_t sV = 0;                           // fp32 [2][BV][PL]      conv(v) of the slice
+    static constexpr size_t sO = sV + 4 * 2 * VT;             // fp32 [kORing][BV][PL] pre-norm output
+    static constexpr size_t sRawV = sO + 4 * kORing * VT;     // bf16 [2][64][BV]      raw v of the slice
+    static constexpr size_t sZ = sRawV + 2 * 2 * kC * BV;     // bf16 [2][64][BV]      z of the slice
+    static constexpr size_t sRstd = sZ + 2 * 2 * kC * BV;     // fp32 [2][64]          gated-norm 1/rms per row
+    static constexpr size_t sCW = sRstd + 4 * 2 * kC;         // fp32 [BV][4]          conv taps of the v channels
+    static constexpr size_t sNW = sCW + 4 * 4 * BV;           // fp32 [BV]             gated-norm weights
     static constexpr size_t bytes = sNW + 4 * BV;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// Global data of one pipeline step, fetched by the helper waves into registers
-// while the chain waves compute: the chunk's operands (q^, k^ [64][128]: 2048
-// 16-byte pieces contiguous in the workspace; T diag(beta), P: 384 pieces
-// each; the decay vectors: 32 pieces), a later chunk's raw v slice and an
-// earlier chunk's z slice (8*BV pieces each).  k^T is rebuilt in LDS.
-
-template <int NT>
-struct PF {
-    static constexpr int BV = 16 * NT;
-    static constexpr int NH = (4 - NT) * 64;          // helper threads
-    static constexpr int NV = 8 * BV;                 // 16-byte pieces of one 64-row slice
-    static constexpr int NQK = (2048 + NH - 1) / NH;  // q^, k^ pieces per helper
-    static constexpr int NTP = (800 + NH - 1) / NH;   // T diag(beta), P, decay-vector pieces per helper
-    static constexpr int NVZ = (NV + NH - 1) / NH;    // raw-v (and z) pieces per helper
+// Operand registers of one chain wave: the fragments of the chunk being
+// computed.  Each set is overwritten with the next chunk's fragments right
+// after its last use in the current chunk.
+struct ChainFrags {
+    half8 k[16], q[16], kt[16], tb[6], p[6];
+    float4 egx[4], ego[4], egc[4];  // e^{G} (for X and for O), e^{G_C - G}: rows 16 I + 4 lq .. +3
+    float dC;                       // e^{G_C}
 };
 
-// Registers of one pipeline step (helpers).
-template <int NT>
-struct Stage {
-    u32x4 qk[PF<NT>::NQK], tp[PF<NT>::NTP], rv[PF<NT>::NVZ], z[PF<NT>::NVZ];
-};
-
-// Issue the loads of one pipeline step: operands of chunk c_op, raw v of chunk
-// c_v, z of chunk c_z.  Rows of chunks outside [0, nch) or past T are read from
-// a valid row and zeroed when stored, so issuing never waits for a load.
-template <int NT>
-__device__ __forceinline__ void prefetch_issue(const ChainArgs &a, int b, int h, int kh, int sv0, int c_op, int c_v,
-                                               int c_z, int htid, Stage<NT> &st) {
-    using F = PF<NT>;
-    constexpr int NCG = F::BV / 8;
-    const int cop = min(c_op, a.nch - 1);
-    const u32x4 *qk = reinterpret_cast<const u32x4 *>(a.qkw + (((size_t)b * a.nch + cop) * a.Hk + kh) * kQK) + htid;
-    // (pieces past the end re-read the last one)
-    const u32x4 *tp = reinterpret_cast<const u32x4 *>(a.tpw + (((size_t)b * a.nch + cop) * a.Hv + h) * kTP);
+__device__ __forceinline__ void frags_load(ChainFrags &fr, const _Float16 *qkb, const _Float16 *tpb, int lane,
+                                           int lq) {
+    const half8 *qn = reinterpret_cast<const half8 *>(qkb) + lane;
+    const half8 *tn = reinterpret_cast<const half8 *>(tpb) + lane;
+    const float4 *vn = reinterpret_cast<const float4 *>(tpb + kVecOff);
 #pragma unroll
-    for (int u = 0; u < F::NQK; ++u) st.qk[u] = qk[min(F::NH * u, 2047 - htid)];
-#pragma unroll
-    for (int u = 0; u < F::NTP; ++u) st.tp[u] = tp[min(htid + F::NH * u, 799)];
-    const int cg = htid % NCG;
-    const uint16_t *zsrc = a.norm ? a.z : a.v;
-#pragma unroll
-    for (int u = 0; u < F::NVZ; ++u) {
-        const int row = min((htid + F::NH * u) / NCG, kC - 1);
-        const int tv = min(max(c_v, 0) * kC + row, a.T - 1), tz = min(max(c_z, 0) * kC + row, a.T - 1);
-        st.rv[u] = *reinterpret_cast<const u32x4 *>(a.v + (((size_t)b * a.T + tv) * a.Hv + h) * kD + sv0 + 8 * cg);
-        st.z[u] = *reinterpret_cast<const u32x4 *>(zsrc + (((size_t)b * a.T + tz) * a.Hv + h) * kD + sv0 + 8 * cg);
+    for (int f = 0; f < 16; ++f) {
+        fr.q[f] = qn[f * 64];
+        fr.k[f] = qn[(16 + f) * 64];
+        fr.kt[f] = qn[(32 + f) * 64];
     }
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        fr.tb[f] = tn[f * 64];
+        fr.p[f] = tn[(6 + f) * 64];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        fr.egx[u] = vn[4 * u + lq];
+        fr.ego[u] = vn[4 * u + lq];
+        fr.egc[u] = vn[16 + 4 * u + lq];
+    }
+    fr.dC = reinterpret_cast<const float *>(tpb + kVecOff)[2 * kC];
 }
 
-// Store one pipeline step's registers into LDS: operands, raw v into buffer
-// rv_buf, z.
-template <int NT>
-__device__ __forceinline__ void prefetch_store(unsigned char *smem, int htid, int rv_buf, int c_v, int c_z, int T,
-                                               const Stage<NT> &st) {
-    using L = ChainLds<NT>;
-    using F = PF<NT>;
-    _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + L::sQ);
-    _Float16 *sTb = reinterpret_cast<_Float16 *>(smem + L::sTb);
-    // q^ then k^ (both [64][P128], adjacent)
-#pragma unroll
-    for (int u = 0; u < F::NQK; ++u) {
-        const int i = htid + F::NH * u;
-        if (i < 2048) *reinterpret_cast<u32x4 *>(sQ + (i >> 4) * P128 + (i & 15) * 8) = st.qk[u];
-    }
-    // T diag(beta) then P (both [64][P64], adjacent), then the decay vectors
-#pragma unroll
-    for (int u = 0; u < F::NTP; ++u) {
-        const int i = htid + F::NH * u;
-        if (i < 768) {
-            const int j = i % 384;
-            const int off = (i >= 384 ? kC * P64 : 0) +
-                            (j < 128 ? (j >> 2) * P64 + (j & 3) * 8 : (32 + ((j - 128) >> 3)) * P64 + ((j - 128) & 7) * 8);
-            *reinterpret_cast<u32x4 *>(sTb + off) = st.tp[u];
-        } else if (i < 800) {
-            reinterpret_cast<u32x4 *>(smem + L::sEG)[i - 768] = st.tp[u];
-        }
-    }
-    u32x4 *sRawV = reinterpret_cast<u32x4 *>(smem + L::sRawV) + rv_buf * F::NV;
-    u32x4 *sZ = reinterpret_cast<u32x4 *>(smem + L::sZ);
-    constexpr int NCG = F::BV / 8;
-#pragma unroll
-    for (int u = 0; u < F::NVZ; ++u) {
-        const int i = htid + F::NH * u;
-        if (i < F::NV) {
-            const int row = i / NCG;
-            const bool okv = c_v >= 0 && c_v * kC + row < T, okz = c_z >= 0 && c_z * kC + row < T;
-            sRawV[i] = okv ? st.rv[u] : u32x4{0u, 0u, 0u, 0u};
-            sZ[i] = okz ? st.z[u] : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-}
+// One chunk of the state chain for one 16-column tile (a chain wave):
+//   X = V - e^G (K S);  Delta = T diag(beta) X;  O = e^G (Q S) + P Delta (to sOc);
+//   S = e^{G_C} S + K^T (e^{G_C - G} Delta).
+// S holds the tile in the accumulator layout (key-row tiles ti = 0..7).  qkn /
+// tpn are the next chunk's blocks: each fragment set is reloaded from them
+// after its last use here.  Scheduling barriers keep each phase's MFMAs
+// ahead of the reloads that overwrite their operands.
+__device__ __forceinline__ void chain_step(ChainFrags &fr, floatx4 (&S)[8], const _Float16 *qkn,
+                                           const _Float16 *tpn, const float *sVc, float *sOc, int lane, int jc,
+                                           int lq) {
+    const half8 *qn = reinterpret_cast<const half8 *>(qkn) + lane;
+    const half8 *tn = reinterpret_cast<const half8 *>(tpn) + lane;
+    const float4 *vn = reinterpret_cast<const float4 *>(tpn + kVecOff);
 
-// k^T in LDS from k^ (helpers): sKT[d][tpos] = sK[t][kpos], where both axes
-// keep their 32-block permutation of the stored contraction index.  A unit is
-// 4 consecutive tokens x one 4-group of keys (contiguous in both layouts).
-template <int NT>
-__device__ __forceinline__ void transpose_k(unsigned char *smem, int htid) {
-    using L = ChainLds<NT>;
-    const _Float16 *sK = reinterpret_cast<const _Float16 *>(smem + L::sK);
-    _Float16 *sKT = reinterpret_cast<_Float16 *>(smem + L::sKT);
-    constexpr int NH = (4 - NT) * 64;
-    for (int unit = htid; unit < 16 * 32; unit += NH) {
-        const int tg = unit & 15, kg = unit >> 4;  // token 4-group (0..15), key 4-group (0..31)
-        // stored positions: key 4-group kg of block kg/8 sits at 32*(kg/8) + kpos(kg%8); same for tokens
-        const int kp = 32 * (kg >> 3) + kpos(kg & 7), tp = 32 * (tg >> 3) + kpos(tg & 7);
-        half4 r[4];
+    float4 vv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = lds_half4(sK + (4 * tg + i) * P128 + kp);
-        // natural key index of stored position kp+j: 4*kg + j
+    for (int I = 0; I < 4; ++I) vv[I] = *reinterpret_cast<const float4 *>(sVc + jc * PL + 16 * I + 4 * lq);
+    half8 Sb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<half4 *>(sKT + (4 * kg + j) * P64 + tp) = half4{r[0][j], r[1][j], r[2][j], r[3][j]};
+    for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = pack_tiles(S[2 * s2], S[2 * s2 + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // K S (token-row tiles I, contraction over keys; k-step outermost: four chains in flight)
+    floatx4 ks[4] = {};
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) ks[I] = mfma16x16x32(fr.k[4 * I + s2], Sb[s2], ks[I]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) fr.k[f] = qn[(16 + f) * 64];
+
+    // X = V - e^G K S
+    floatx4 X[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        X[I][0] = vv[I].x - fr.egx[I].x * ks[I][0];
+        X[I][1] = vv[I].y - fr.egx[I].y * ks[I][1];
+        X[I][2] = vv[I].z - fr.egx[I].z * ks[I][2];
+        X[I][3] = vv[I].w - fr.egx[I].w * ks[I][3];
     }
+    const half8 Xb[2] = {pack_tiles(X[0], X[1]), pack_tiles(X[2], X[3])};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fr.egx[u] = vn[4 * u + lq];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Delta = T diag(beta) X  (lower triangular: 32-row block s2 uses k-steps <= s2)
+    half8 Db[2], Dsb[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+        if (s2 == 0) {
+            d0 = mfma16x16x32(fr.tb[0], Xb[0], d0);
+            d1 = mfma16x16x32(fr.tb[1], Xb[0], d1);
+        } else {
+            d0 = mfma16x16x32(fr.tb[2], Xb[0], d0);
+            d0 = mfma16x16x32(fr.tb[3], Xb[1], d0);
+            d1 = mfma16x16x32(fr.tb[4], Xb[0], d1);
+            d1 = mfma16x16x32(fr.tb[5], Xb[1], d1);
+        }
+        Db[s2] = pack_tiles(d0, d1);
+        const float4 c0 = fr.egc[2 * s2], c1 = fr.egc[2 * s2 + 1];
+        Dsb[s2] = half8{(_Float16)(d0[0] * c0.x), (_Float16)(d0[1] * c0.y), (_Float16)(d0[2] * c0.z),
+                        (_Float16)(d0[3] * c0.w), (_Float16)(d1[0] * c1.x), (_Float16)(d1[1] * c1.y),
+                        (_Float16)(d1[2] * c1.z), (_Float16)(d1[3] * c1.w)};
+    }
+    // the decay of the old state, ahead of the update at the end
+#pragma unroll
+    for (int ti = 0; ti < 8; ++ti) S[ti] = S[ti] * fr.dC;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 6; ++f) fr.tb[f] = tn[f * 64];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fr.egc[u] = vn[16 + 4 * u + lq];
+    fr.dC = reinterpret_cast<const float *>(tpn + kVecOff)[2 * kC];
+
+    // Q S
+    floatx4 qs[4] = {};
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) qs[I] = mfma16x16x32(fr.q[4 * I + s2], Sb[s2], qs[I]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) fr.q[f] = qn[f * 64];
+
+    // O = e^G Q S + P Delta, to LDS (column-major: four consecutive rows per lane)
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        floatx4 ot = {qs[I][0] * fr.ego[I].x, qs[I][1] * fr.ego[I].y, qs[I][2] * fr.ego[I].z,
+                      qs[I][3] * fr.ego[I].w};
+        if (I < 2) {
+            ot = mfma16x16x32(fr.p[I], Db[0], ot);
+        } else {
+            ot = mfma16x16x32(fr.p[2 + 2 * (I - 2)], Db[0], ot);
+            ot = mfma16x16x32(fr.p[3 + 2 * (I - 2)], Db[1], ot);
+        }
+        *reinterpret_cast<float4 *>(sOc + jc * PL + 16 * I + 4 * lq) = make_float4(ot[0], ot[1], ot[2], ot[3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 6; ++f) fr.p[f] = tn[(6 + f) * 64];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fr.ego[u] = vn[4 * u + lq];
+
+    // S += K^T Delta~  (key-row tiles ti, contraction over tokens)
+#pragma unroll
+    for (int ti = 0; ti < 8; ++ti) {
+        floatx4 acc = S[ti];
+        acc = mfma16x16x32(fr.kt[2 * ti], Dsb[0], acc);
+        acc = mfma16x16x32(fr.kt[2 * ti + 1], Dsb[1], acc);
+        S[ti] = acc;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) fr.kt[f] = qn[(32 + f) * 64];
 }
 
 __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, uint32_t tag, unsigned int *err,
@@ -545,134 +620,28 @@ __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, u
     return w;
 }
 
-// One chunk of the state chain for one 16-column tile (chain waves), first
-// part: K S, X, Delta, O (to sOc).  S holds the tile in the accumulator layout
-// (key-row tiles ti = 0..7).  Every MFMA A operand is a single 16-byte LDS read
-// thanks to the permuted storage of the contraction index.
+// Raw v (of one chunk) and z (of another) for the slice, in registers: piece
+// i = lane + 64 u is row i / NCG, 8 columns at 8 (i % NCG).
 template <int NT>
-__device__ __forceinline__ void chain_chunk_a(unsigned char *smem, const floatx4 (&S)[8], const float *sVc,
-                                              float *sOc, int jc, int l16, int lq, half8 (&Dsb)[2]) {
-    using L = ChainLds<NT>;
-    constexpr int PV = L::PV;
-    const _Float16 *sQ = reinterpret_cast<const _Float16 *>(smem + L::sQ);
-    const _Float16 *sK = reinterpret_cast<const _Float16 *>(smem + L::sK);
-    const _Float16 *sTb = reinterpret_cast<const _Float16 *>(smem + L::sTb);
-    const _Float16 *sP = reinterpret_cast<const _Float16 *>(smem + L::sP);
-    const float *sEG = reinterpret_cast<const float *>(smem + L::sEG);
-    const float *sEGC = sEG + kC;
-
-    half8 Sb[4];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = pack_tiles(S[2 * s2], S[2 * s2 + 1]);
-
-    half8 fr[16];  // A-operand fragments of one phase, loaded together
-    // K S (token-row tiles I, contraction over key dims), then X = V - e^G K S
-#pragma unroll
-    for (int f = 0; f < 16; ++f) fr[f] = lds_half8(sK + (16 * (f >> 2) + l16) * P128 + 32 * (f & 3) + 8 * lq);
-    floatx4 X[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        floatx4 ks = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) ks = mfma16x16x32(fr[4 * I + s2], Sb[s2], ks);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * I + 4 * lq + e;
-            X[I][e] = sVc[row * PV + jc] - sEG[row] * ks[e];
-        }
-    }
-    const half8 Xb[2] = {pack_tiles(X[0], X[1]), pack_tiles(X[2], X[3])};
-
-    // Delta = T diag(beta) X  (lower triangular: 32-row block s2 uses k-steps <= s2)
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-        const int s2 = f < 2 ? 0 : 1, hh = f < 2 ? f : (f - 2) >> 1, k2 = f < 2 ? 0 : (f - 2) & 1;
-        fr[f] = lds_half8(sTb + (32 * s2 + 16 * hh + l16) * P64 + 32 * k2 + 8 * lq);
-    }
-    half8 Db[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
-        if (s2 == 0) {
-            d0 = mfma16x16x32(fr[0], Xb[0], d0);
-            d1 = mfma16x16x32(fr[1], Xb[0], d1);
-        } else {
-            d0 = mfma16x16x32(fr[2], Xb[0], d0);
-            d0 = mfma16x16x32(fr[3], Xb[1], d0);
-            d1 = mfma16x16x32(fr[4], Xb[0], d1);
-            d1 = mfma16x16x32(fr[5], Xb[1], d1);
-        }
-        Db[s2] = pack_tiles(d0, d1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            Dsb[s2][e] = static_cast<_Float16>(d0[e] * sEGC[32 * s2 + 4 * lq + e]);
-            Dsb[s2][4 + e] = static_cast<_Float16>(d1[e] * sEGC[32 * s2 + 16 + 4 * lq + e]);
-        }
-    }
-
-    // O = e^G Q S + P Delta
-#pragma unroll
-    for (int f = 0; f < 16; ++f) fr[f] = lds_half8(sQ + (16 * (f >> 2) + l16) * P128 + 32 * (f & 3) + 8 * lq);
-    half8 fp[6];
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-        const int I = f < 2 ? f : 2 + ((f - 2) >> 1), s2 = f < 2 ? 0 : (f - 2) & 1;
-        fp[f] = lds_half8(sP + (16 * I + l16) * P64 + 32 * s2 + 8 * lq);
-    }
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        floatx4 qs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) qs = mfma16x16x32(fr[4 * I + s2], Sb[s2], qs);
-        floatx4 ot;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ot[e] = qs[e] * sEG[16 * I + 4 * lq + e];
-        if (I < 2) {
-            ot = mfma16x16x32(fp[I], Db[0], ot);
-        } else {
-            ot = mfma16x16x32(fp[2 + 2 * (I - 2)], Db[0], ot);
-            ot = mfma16x16x32(fp[3 + 2 * (I - 2)], Db[1], ot);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sOc[(16 * I + 4 * lq + e) * PV + jc] = ot[e];
-    }
-
-}
-
-// Second part: S = e^{G_C} S + K^T Delta~  (key-row tiles ti, contraction over
-// tokens).  Needs k^T of the chunk in LDS.
-template <int NT>
-__device__ __forceinline__ void chain_chunk_b(unsigned char *smem, floatx4 (&S)[8], const half8 (&Dsb)[2], int l16,
-                                              int lq) {
-    using L = ChainLds<NT>;
-    const _Float16 *sKT = reinterpret_cast<const _Float16 *>(smem + L::sKT);
-    const float *sEG = reinterpret_cast<const float *>(smem + L::sEG);
-    half8 fr[16];
-#pragma unroll
-    for (int f = 0; f < 16; ++f) fr[f] = lds_half8(sKT + (16 * (f >> 1) + l16) * P64 + 32 * (f & 1) + 8 * lq);
-    const float dC = sEG[kC - 1];
-#pragma unroll
-    for (int ti = 0; ti < 8; ++ti) {
-        floatx4 acc = S[ti] * dC;
-        acc = mfma16x16x32(fr[2 * ti], Dsb[0], acc);
-        acc = mfma16x16x32(fr[2 * ti + 1], Dsb[1], acc);
-        S[ti] = acc;
-    }
-}
+struct VZStage {
+    static constexpr int NCG = 2 * NT;  // 8-column groups per row
+    static constexpr int N = NCG;       // pieces per lane: 64 rows * NCG / 64
+    u32x4 v[N], z[N];
+};
 
 template <int NT>
-__global__ __launch_bounds__(256) void chain_kernel(ChainArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chain_kernel(ChainArgs a) {
     using L = ChainLds<NT>;
-    using F = PF<NT>;
-    constexpr int BV = L::BV, PV = L::PV;
+    using ST = VZStage<NT>;
+    constexpr int BV = L::BV, VT = L::VT;
     constexpr int NSL = kTiles / NT;
-    constexpr int NCG = BV / 8;  // 8-column groups per slice row
-    constexpr int NH = F::NH;    // helper threads
+    constexpr int NCG = ST::NCG;
+    constexpr int NG = 3 - NT;  // gate waves
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *sV = reinterpret_cast<float *>(smem + L::sV);
     float *sO = reinterpret_cast<float *>(smem + L::sO);
-    const uint16_t *sRawV = reinterpret_cast<const uint16_t *>(smem + L::sRawV);
-    const uint16_t *sZ = reinterpret_cast<const uint16_t *>(smem + L::sZ);
+    uint16_t *sRawV = reinterpret_cast<uint16_t *>(smem + L::sRawV);
+    uint16_t *sZ = reinterpret_cast<uint16_t *>(smem + L::sZ);
     float *sRstd = reinterpret_cast<float *>(smem + L::sRstd);
     float *sCW = reinterpret_cast<float *>(smem + L::sCW);
     float *sNW = reinterpret_cast<float *>(smem + L::sNW);
@@ -680,10 +649,10 @@ __global__ __launch_bounds__(256) void chain_kernel(ChainArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches are scalar
     const int l16 = lane & 15, lq = lane >> 4;
-    const bool is_chain = wave < NT;
-    const int htid = tid - NT * 64;                       // helper index
-    const int hcg = (htid >= 0 ? htid : 0) % NCG;         // fixed column group of a helper (NH % NCG == 0)
-
+    // roles: waves 0..NT-1 chain; wave NT loads raw v / z, converts v and runs the
+    // norm exchange; the remaining waves apply the gated norm and store o
+    const bool is_chain = wave < NT, is_lm = wave == NT;
+    const int gtid = tid - 64 * (NT + 1);  // gate-thread index (valid on gate waves)
     int broken = 0;
     __shared__ int s_item;
     // Work items (chain, slice) come from eight queues, one per XCD: chain c
@@ -714,79 +683,30 @@ __global__ __launch_bounds__(256) void chain_kernel(ChainArgs a) {
             s_item = item;
         }
         __syncthreads();
-        const int item = s_item;
+        const int item = __builtin_amdgcn_readfirstlane(s_item);  // uniform: addresses stay scalar
         __syncthreads();
         if (item < 0) break;
         const int chain = item / NSL, s = item % NSL;
         const int b = chain / a.Hv, h = chain % a.Hv, kh = h / a.r;
         const int sv0 = s * BV;
-        const int jc = 16 * wave + l16;  // column of a chain-wave lane inside the slice
-        const int hch = 2 * a.Hk * kD + h * kD + sv0 + hcg * 8;  // conv channel of a helper's 8 columns
+        const int last = a.nch + kLag;  // iterations 0..last: chunk c, norm of c-kLag, store of c-kLag-1
 
-        // conv + SiLU of the slice of v for chunk cc, from raw rows in LDS, into sV[cc & 1]
-        auto conv_v = [&](int cc) {
-            float *dst = sV + (cc & 1) * kC * PV;
-            const uint16_t *cur = sRawV + (cc & 1) * kC * BV;
-            const uint16_t *prev = sRawV + ((cc + 1) & 1) * kC * BV;  // chunk cc-1: the last three rows are the halo
-            const float *hw = sCW + hcg * 8 * 4;                       // [8 channels][4 taps]
-#pragma unroll 1
-            for (int it = htid; it < kC * NCG; it += NH) {
-                const int row = it / NCG;
-                float x[4][8];
+        // weights of the slice
+        if (tid >= 64 * NT && tid < 64 * NT + BV) {
+            const int j = tid - 64 * NT, chn = 2 * a.Hk * kD + h * kD + sv0 + j;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r2 = row - 3 + j;
-                    uint4 rw = make_uint4(0, 0, 0, 0);
-                    if (j == 3 || a.conv) {
-                        if (r2 >= 0)
-                            rw = *reinterpret_cast<const uint4 *>(cur + r2 * BV + hcg * 8);
-                        else if (cc > 0)
-                            rw = *reinterpret_cast<const uint4 *>(prev + (kC + r2) * BV + hcg * 8);
-                        else if (a.conv_state_in)
-                            rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + r2)) * a.Cc + hch);
-                    }
-                    unpack_bf16x8(rw, x[j]);
-                }
-                float u[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    u[e] = a.conv ? silu(hw[4 * e] * x[0][e] + hw[4 * e + 1] * x[1][e] + hw[4 * e + 2] * x[2][e] +
-                                         hw[4 * e + 3] * x[3][e])
-                                  : x[3][e];
-                float4 *d4 = reinterpret_cast<float4 *>(dst + row * PV + hcg * 8);
-                d4[0] = make_float4(u[0], u[1], u[2], u[3]);
-                d4[1] = make_float4(u[4], u[5], u[6], u[7]);
-            }
-        };
-
-        // ---- prologue: weights, operands of chunk 0, raw v of chunks 0 and 1, v of chunk 0
-        if (htid >= 0 && htid < BV) {
-            const int chn = 2 * a.Hk * kD + h * kD + sv0 + htid;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sCW[htid * 4 + j] = a.conv ? bf16_to_f32(a.conv_w[(size_t)chn * 4 + j]) : 0.0f;
-            sNW[htid] = a.norm ? bf16_to_f32(a.norm_w[sv0 + htid]) : 1.0f;
+            for (int t4 = 0; t4 < 4; ++t4) sCW[j * 4 + t4] = a.conv ? bf16_to_f32(a.conv_w[(size_t)chn * 4 + t4]) : 0.0f;
+            sNW[j] = a.norm ? bf16_to_f32(a.norm_w[sv0 + j]) : 1.0f;
         }
-        if (!is_chain) {
-            Stage<NT> st0;
-            prefetch_issue<NT>(a, b, h, kh, sv0, 0, 0, -1, htid, st0);
-            prefetch_store<NT>(smem, htid, 0, 0, -1, a.T, st0);
-            prefetch_issue<NT>(a, b, h, kh, sv0, 0, 1, -1, htid, st0);  // (operands of chunk 0 again: harmless)
-            prefetch_store<NT>(smem, htid, 1, 1, -1, a.T, st0);
-        }
-        lds_barrier();  // weights and raw v visible to every helper
-        if (!is_chain) conv_v(0);
         lds_barrier();
 
-        // ---- pipeline.  Chain waves and helpers run separate loops (the role test
-        // is wave-uniform, so each wave takes one branch); both execute exactly
-        // three barriers per iteration.  In iteration c the chain waves compute chunk c
-        // into sO[c % 4]; the helpers publish the row sums of chunk c-1, finish the
-        // norm statistics of chunk c-2, apply the norm to chunk c-3, convert v of
-        // chunk c+1, and fetch the operands of chunk c+1, the raw v of chunk c+2
-        // and the z of chunk c-2 -- every global access gets a full iteration --
-        // and rebuild k^T of chunk c (needed by the chain's state update).
-        const int last = a.nch + 3;
         if (is_chain) {
+            const int jc = 16 * wave + l16;  // column of this lane inside the slice
+            const size_t qk_stride = (size_t)a.Hk * kQKF, tp_stride = (size_t)a.Hv * kTPF;
+            const _Float16 *qk0 = a.qkf + ((size_t)b * a.nch * a.Hk + kh) * kQKF;
+            const _Float16 *tp0 = a.tpf + ((size_t)b * a.nch * a.Hv + h) * kTPF;
+            ChainFrags fr;
+            frags_load(fr, qk0, tp0, lane, lq);
             floatx4 S[8];
             {
                 const float *src = a.state_in ? a.state_in + (size_t)chain * kD * kD : nullptr;
@@ -796,96 +716,136 @@ __global__ __launch_bounds__(256) void chain_kernel(ChainArgs a) {
                     for (int e = 0; e < 4; ++e)
                         S[ti][e] = src ? src[(size_t)(16 * ti + 4 * lq + e) * kD + sv0 + jc] : 0.0f;
             }
+            lds_barrier();  // (prologue: v of chunk 0 converted)
             for (int c = 0; c <= last; ++c) {
-                half8 Dsb[2];
-                if (c < a.nch)
-                    chain_chunk_a<NT>(smem, S, sV + (c & 1) * kC * PV, sO + (c % 5) * kC * PV, jc, l16, lq, Dsb);
-                lds_barrier();  // k^T of chunk c built
-                if (c < a.nch) chain_chunk_b<NT>(smem, S, Dsb, l16, lq);
-                lds_barrier();  // chunk c done: operand buffers may be refilled
-                lds_barrier();  // operands of chunk c+1 in place
+                if (c < a.nch) {
+                    const int cn = c + 1 < a.nch ? c + 1 : c;  // (the last chunk re-reads its own blocks)
+                    chain_step(fr, S, qk0 + cn * qk_stride, tp0 + cn * tp_stride, sV + (c & 1) * VT,
+                               sO + (c % kORing) * VT, lane, jc, lq);
+                }
+                lds_barrier();
             }
 #pragma unroll
             for (int ti = 0; ti < 8; ++ti)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     a.state_out[(size_t)chain * kD * kD + (size_t)(16 * ti + 4 * lq + e) * kD + sv0 + jc] = S[ti][e];
-        } else {
-            Stage<NT> pf;
+        } else if (is_lm) {
+            const uint16_t *zsrc = a.norm ? a.z : a.v;
+            // issue the loads of raw v rows of chunk cv and z rows of chunk cz (rows are clamped to
+            // valid tokens here and zeroed when stored, so issuing never waits for a load)
+            auto stage_issue = [&](ST &st, int cv, int cz) __attribute__((always_inline)) {
+#pragma unroll
+                for (int u = 0; u < ST::N; ++u) {
+                    const int i = lane + 64 * u, row = i / NCG, cg = i % NCG;
+                    const int tv = min(max(cv, 0) * kC + row, a.T - 1), tz = min(max(cz, 0) * kC + row, a.T - 1);
+                    st.v[u] = *reinterpret_cast<const u32x4 *>(a.v + (((size_t)b * a.T + tv) * a.Hv + h) * kD + sv0 + 8 * cg);
+                    st.z[u] = *reinterpret_cast<const u32x4 *>(zsrc + (((size_t)b * a.T + tz) * a.Hv + h) * kD + sv0 + 8 * cg);
+                }
+            };
+            auto stage_store = [&](const ST &st, int cv, int cz) __attribute__((always_inline)) {
+                u32x4 *dv = reinterpret_cast<u32x4 *>(sRawV + (cv & 1) * kC * BV);
+                u32x4 *dz = reinterpret_cast<u32x4 *>(sZ + (cz & 1) * kC * BV);
+#pragma unroll
+                for (int u = 0; u < ST::N; ++u) {
+                    const int i = lane + 64 * u, row = i / NCG;
+                    const bool okv = cv >= 0 && cv * kC + row < a.T, okz = cz >= 0 && cz * kC + row < a.T;
+                    dv[i] = okv ? st.v[u] : u32x4{0u, 0u, 0u, 0u};
+                    dz[i] = okz ? st.z[u] : u32x4{0u, 0u, 0u, 0u};
+                }
+            };
+            // conv + SiLU of the slice of v for chunk cc, from raw rows in LDS, into sV[cc & 1]
+            auto conv_v = [&](int cc) __attribute__((always_inline)) {
+                float *dst = sV + (cc & 1) * VT;
+                const uint16_t *cur = sRawV + (cc & 1) * kC * BV;
+                const uint16_t *prev = sRawV + ((cc + 1) & 1) * kC * BV;  // chunk cc-1: its last three rows are the halo
+#pragma unroll
+                for (int u = 0; u < NCG; ++u) {
+                    const int it = lane + 64 * u, row = it / NCG, cg = it % NCG;
+                    float x[4][8];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r2 = row - 3 + j;
+                        uint4 rw = make_uint4(0, 0, 0, 0);
+                        if (j == 3 || a.conv) {
+                            if (r2 >= 0)
+                                rw = *reinterpret_cast<const uint4 *>(cur + r2 * BV + cg * 8);
+                            else if (cc > 0)
+                                rw = *reinterpret_cast<const uint4 *>(prev + (kC + r2) * BV + cg * 8);
+                            else if (a.conv_state_in)
+                                rw = *reinterpret_cast<const uint4 *>(
+                                    a.conv_state_in + ((size_t)b * 3 + (3 + r2)) * a.Cc + 2 * a.Hk * kD + h * kD + sv0 + cg * 8);
+                        }
+                        unpack_bf16x8(rw, x[j]);
+                    }
+                    const float *hw = sCW + cg * 8 * 4;  // [8 channels][4 taps]
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float u8 = a.conv ? silu(hw[4 * e] * x[0][e] + hw[4 * e + 1] * x[1][e] +
+                                                       hw[4 * e + 2] * x[2][e] + hw[4 * e + 3] * x[3][e])
+                                                : x[3][e];
+                        dst[(cg * 8 + e) * PL + row] = u8;
+                    }
+                }
+            };
             unsigned long long mbw[NSL];
-            unsigned long long *mrow = a.mbox + (size_t)chain * kTiles * kRing * kC + htid;  // row htid (< 64)
-            for (int c = 0; c <= last; ++c) {
-                const bool fetch = c + 1 < a.nch || (c - 3 >= 0 && c - 3 < a.nch);
-                // partial sums of chunk c-3 from every slice: issue now, use at the end
-                const bool want_rstd = a.norm && htid < kC && c >= 3 && c - 3 < a.nch;
+            unsigned long long *mrow = a.mbox + (size_t)chain * kTiles * kRing * kC + lane;  // row = lane
+            auto lm_iter = [&](int c, ST &st) __attribute__((always_inline)) {
+                // partial sums of chunk c-kLag from every slice: issue now, use at the end
+                const bool want_rstd = a.norm && c >= kLag && c - kLag < a.nch;
                 if (want_rstd) {
 #pragma unroll
                     for (int sib = 0; sib < NSL; ++sib)
-                        mbw[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + ((c - 3) % kRing)) * kC,
+                        mbw[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + ((c - kLag) % kRing)) * kC,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                if (fetch) prefetch_issue<NT>(a, b, h, kh, sv0, c + 1, c + 2, c - 3, htid, pf);
-                if (c < a.nch) transpose_k<NT>(smem, htid);  // k^ of chunk c is in LDS
-                lds_barrier();                                // k^T of chunk c built
+                // raw v of chunk c+1 and z of chunk c-kLag (loaded two iterations ago) to LDS,
+                // then the loads for two iterations ahead into the same registers
+                stage_store(st, c + 1, c - kLag);
+                stage_issue(st, c + 3, c + 2 - kLag);
+                if (c + 1 < a.nch) conv_v(c + 1);
                 // row sums of chunk c-1 over this slice's columns -> mailbox
-                if (a.norm && c >= 1 && c - 1 < a.nch && htid >= NH - kC) {
-                    const int row = htid - (NH - kC);
-                    const float *src = sO + ((c - 1) % 5) * kC * PV + row * PV;
+                if (a.norm && c >= 1 && c - 1 < a.nch) {
+                    const float *src = sO + ((c - 1) % kORing) * VT + lane;
                     float ss = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < BV; j += 4) {
-                        const float4 v4 = *reinterpret_cast<const float4 *>(src + j);
-                        ss += v4.x * v4.x + v4.y * v4.y + v4.z * v4.z + v4.w * v4.w;
-                    }
-                    unsigned long long *mb =
-                        a.mbox + (((size_t)chain * kTiles + s) * kRing + ((c - 1) % kRing)) * kC + row;
+                    for (int j = 0; j < BV; ++j) ss += src[j * PL] * src[j * PL];
+                    unsigned long long *mb = a.mbox + (((size_t)chain * kTiles + s) * kRing + ((c - 1) % kRing)) * kC + lane;
                     __hip_atomic_store(mb, ((unsigned long long)(uint32_t)c << 32) | __float_as_uint(ss),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                // gated RMSNorm + store of chunk c-4
-                if (c >= 4 && c - 4 < a.nch) {
-                    const int oc = c - 4;
-                    const float *src = sO + (oc % 5) * kC * PV;
-                    const float *rs = sRstd + (oc & 1) * kC;
-#pragma unroll 1
-                    for (int it = htid; it < kC * NCG; it += NH) {
-                        const int row = it / NCG;
-                        const int t = oc * kC + row;
-                        if (t >= a.T) continue;
-                        const float4 o0 = *reinterpret_cast<const float4 *>(src + row * PV + hcg * 8);
-                        const float4 o1 = *reinterpret_cast<const float4 *>(src + row * PV + hcg * 8 + 4);
-                        float y[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
-                        if (a.norm) {
-                            float zf[8];
-                            unpack_bf16x8(*reinterpret_cast<const uint4 *>(sZ + row * BV + hcg * 8), zf);
-                            const float rstd = rs[row];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) y[e] = sNW[hcg * 8 + e] * (y[e] * rstd) * silu(zf[e]);
-                        }
-                        *reinterpret_cast<uint4 *>(a.o + (((size_t)b * a.T + t) * a.Hv + h) * kD + sv0 + hcg * 8) =
-                            pack_bf16x8(y);
-                    }
-                }
-                if (c + 1 < a.nch) conv_v(c + 1);
-                // 1/rms of chunk c-3's rows
+                // 1/rms of chunk c-kLag's rows
                 if (want_rstd) {
                     float tot = 0.0f;
 #pragma unroll
                     for (int sib = 0; sib < NSL; ++sib) {
-                        if ((uint32_t)(mbw[sib] >> 32) != (uint32_t)(c - 2))
-                            mbw[sib] = spin_load(mrow + ((size_t)sib * kRing + ((c - 3) % kRing)) * kC,
-                                                 (uint32_t)(c - 2), a.err, broken);
+                        if ((uint32_t)(mbw[sib] >> 32) != (uint32_t)(c - kLag + 1))
+                            mbw[sib] = spin_load(mrow + ((size_t)sib * kRing + ((c - kLag) % kRing)) * kC,
+                                                 (uint32_t)(c - kLag + 1), a.err, broken);
                         tot += __uint_as_float((uint32_t)mbw[sib]);
                     }
-                    sRstd[((c - 3) & 1) * kC + htid] = 1.0f / sqrtf(tot * (1.0f / kD) + a.eps_norm);
+                    sRstd[((c - kLag) & 1) * kC + lane] = 1.0f / sqrtf(tot * (1.0f / kD) + a.eps_norm);
                 }
+            };
+            // prologue: raw v of chunk 0 -> LDS -> conv; loads of the first two stages
+            ST st0, st1;
+            stage_issue(st0, 0, -1);
+            stage_store(st0, 0, -1);
+            conv_v(0);
+            stage_issue(st0, 1, -kLag);
+            stage_issue(st1, 2, 1 - kLag);
+            lds_barrier();
+            for (int c = 0; c <= last; c += 2) {
+                lm_iter(c, st0);
                 lds_barrier();
-                if (fetch) prefetch_store<NT>(smem, htid, c & 1, c + 2, c - 3, a.T, pf);
-                lds_barrier();
+                if (c + 1 <= last) {
+                    lm_iter(c + 1, st1);
+                    lds_barrier();
+                }
             }
             // raw v inputs of the last three tokens -> conv state out
-            if (a.conv && a.conv_state_out && htid < 3 * NCG) {
-                const int sidx = htid / NCG, cg = htid % NCG;
+            if (a.conv && a.conv_state_out && lane < 3 * NCG) {
+                const int sidx = lane / NCG, cg = lane % NCG;
                 const int tau = a.T - 3 + sidx;
                 const int ch = 2 * a.Hk * kD + h * kD + sv0 + cg * 8;
                 uint4 rw = make_uint4(0, 0, 0, 0);
@@ -894,6 +854,36 @@ __global__ __launch_bounds__(256) void chain_kernel(ChainArgs a) {
                 else if (a.conv_state_in)
                     rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + tau)) * a.Cc + ch);
                 *reinterpret_cast<uint4 *>(a.conv_state_out + ((size_t)b * 3 + sidx) * a.Cc + ch) = rw;
+            }
+        } else {
+            // gate waves: gated RMSNorm + store of chunk c-kLag-1
+            lds_barrier();
+            for (int c = 0; c <= last; ++c) {
+                const int oc = c - kLag - 1;
+                if (oc >= 0 && oc < a.nch) {
+                    const float *src = sO + (oc % kORing) * VT;
+                    const float *rs = sRstd + (oc & 1) * kC;
+                    const uint16_t *zt = sZ + (oc & 1) * kC * BV;
+#pragma unroll 1
+                    for (int it = gtid; it < kC * NCG; it += NG * 64) {
+                        const int row = it / NCG, cg = it % NCG;
+                        const int t = oc * kC + row;
+                        if (t >= a.T) continue;
+                        float y[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) y[e] = src[(cg * 8 + e) * PL + row];
+                        if (a.norm) {
+                            float zf[8];
+                            unpack_bf16x8(*reinterpret_cast<const uint4 *>(zt + row * BV + cg * 8), zf);
+                            const float rstd = rs[row];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) y[e] = sNW[cg * 8 + e] * (y[e] * rstd) * silu(zf[e]);
+                        }
+                        *reinterpret_cast<uint4 *>(a.o + (((size_t)b * a.T + t) * a.Hv + h) * kD + sv0 + cg * 8) =
+                            pack_bf16x8(y);
+                    }
+                }
+                lds_barrier();
             }
         }
 
@@ -966,8 +956,8 @@ int plan_prefill(int B, int T, int Hk, int Hv, PrefillPlan *plan) {
     plan->nt = kTiles / nsl;
     plan->bv = 16 * plan->nt;
     plan->nchunks = (T + kC - 1) / kC;
-    plan->qk_bytes = align256((size_t)B * plan->nchunks * Hk * kQK * sizeof(_Float16));
-    plan->tp_bytes = align256((size_t)B * plan->nchunks * Hv * kTP * sizeof(_Float16));
+    plan->qk_bytes = align256((size_t)B * plan->nchunks * Hk * kQKF * sizeof(_Float16));
+    plan->tp_bytes = align256((size_t)B * plan->nchunks * Hv * kTPF * sizeof(_Float16));
     plan->mbox_bytes = align256((size_t)chains * kTiles * kRing * kC * sizeof(unsigned long long)) +
                        align256((size_t)chains * sizeof(unsigned int)) + 256;
     plan->total_bytes = plan->qk_bytes + plan->tp_bytes + plan->mbox_bytes;
@@ -976,8 +966,8 @@ int plan_prefill(int B, int T, int Hk, int Hv, PrefillPlan *plan) {
 
 int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream) {
     unsigned char *ws = static_cast<unsigned char *>(p.workspace);
-    _Float16 *qkw = reinterpret_cast<_Float16 *>(ws);
-    _Float16 *tpw = reinterpret_cast<_Float16 *>(ws + plan.qk_bytes);
+    _Float16 *qkf = reinterpret_cast<_Float16 *>(ws);
+    _Float16 *tpf = reinterpret_cast<_Float16 *>(ws + plan.qk_bytes);
     unsigned char *mb = ws + plan.qk_bytes + plan.tp_bytes;
     const size_t chains = (size_t)p.B * p.Hv;
     const size_t mbox_sz = align256(chains * kTiles * kRing * kC * sizeof(unsigned long long));
@@ -988,7 +978,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     PrepArgs pa;
     pa.q = p.q; pa.k = p.k; pa.conv_w = p.conv_w; pa.conv_state_in = p.conv_state_in;
     pa.g = p.g; pa.beta = p.beta; pa.conv_state_out = p.conv_state_out;
-    pa.qkw = qkw; pa.tpw = tpw;
+    pa.qkf = qkf; pa.tpf = tpf;
     pa.B = p.B; pa.T = p.T; pa.Hk = p.Hk; pa.Hv = p.Hv; pa.r = p.Hv / p.Hk;
     pa.Cc = 2 * p.Hk * kD + p.Hv * kD; pa.conv = p.conv_width == 4; pa.nch = plan.nchunks;
     pa.eps_l2 = p.eps_l2;
@@ -1002,7 +992,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     if (e != hipSuccess) return fail("hipLaunchKernel(chunk_prep_kernel)", e);
 
     ChainArgs a;
-    a.qkw = qkw; a.tpw = tpw;
+    a.qkf = qkf; a.tpf = tpf;
     a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w; a.conv_state_in = p.conv_state_in;
     a.state_in = p.state_in; a.o = p.o; a.conv_state_out = p.conv_state_out; a.state_out = p.state_out;
     a.mbox = reinterpret_cast<unsigned long long *>(mb); a.counters = counters; a.err = err;
