@@ -60,17 +60,8 @@ namespace {
 
 constexpr int kD = 128;        // head width
 constexpr int kC = 64;         // chunk length
-// The gated norm of chunk c-kLag is finished in iteration c (and applied in
-// c+1), so a slice reads its siblings' sums kLag-1 iterations after they were
-// published.  A sibling cannot finish iteration c+kLag-1 before this slice
-// has published chunk c-1, so chunks c-kLag .. c+kLag-1 may be live in the
-// mailbox at once: kRing >= 2 kLag slots.
-constexpr int kLag = 4;
-constexpr int kRing = 8;
-constexpr int kORing = 8;      // pre-norm output tiles kept in LDS (>= kLag + 2)
 constexpr int kTiles = 8;      // 16-column tiles per head
 constexpr uint32_t kSpinLimit = 1u << 20;  // bound of every cross-workgroup wait (~0.3 s)
-static_assert(kRing >= 2 * kLag && kORing >= kLag + 2, "pipeline depth");
 
 // LDS pitches (elements) so that 16-row MFMA fragment reads hit distinct banks.
 constexpr int P128 = kD + 8;   // fp16 rows of 128
@@ -82,20 +73,22 @@ constexpr int PTD = 20;        // fp32 rows of a 16x16 block
 // fragments: fragment f holds, for lane L = l16 + 16 lq, the 8 values of row
 // (tile row) + l16 at contraction indices 32 ks + {4 lq .. 4 lq + 3} and
 // 32 ks + 16 + {4 lq .. 4 lq + 3} -- the rows of two adjacent 16-row
-// accumulator tiles as they sit in one lane, i.e. the contraction index of
-// each 32-block taken in the order 4*(p>>3) + (p&3) + 16*((p>>2)&1).
-//   per (sequence, chunk, key head), kQKF:  q^ f = 0..15 (row tile f>>2, k-step f&3 over keys),
-//                                           k^ f = 16..31 (same), k^T f = 32..47 (key-row tile
-//                                           (f-32)>>1, k-step (f-32)&1 over tokens)
-//   per (sequence, chunk, value head), kTPF: T diag(beta) f = 0..5, P = (Q K^T) o R f = 6..11
-//                                           (lower-triangular 64x64, only the blocks that are
-//                                           not all zero), then fp32 e^{G_i} [64],
-//                                           e^{G_C - G_i} [64], e^{G_C} [4]
+// accumulator tiles as they sit in one lane.
+//   per (sequence, chunk, key head), kQKF:  q^ f = 0..15 and k^ f = 16..31 (row tile f>>2,
+//                                           k-step f&3 over keys)
+//   per (sequence, chunk, value head), kTPF: T diag(beta) f = 0..5 (lower-triangular 64x64,
+//                                           only the blocks that are not all zero), fp32
+//                                           e^{G_i} [64], e^{G_C - G_i} [64], e^{G_C} [4]
+//                                           (1 KB), then P = (Q K^T) o R f = 0..5
+// k^T is never stored: the sequential pass reads it from the k^ fragments in
+// LDS with the transposing LDS read.
 constexpr int kBlk = 256;                              // one 16x16 block (prep staging)
 constexpr int kFrag = 64 * 8;                          // one fragment: 64 lanes x 8 fp16
-constexpr int kQKF = 48 * kFrag;
-constexpr int kVecOff = 12 * kFrag;
-constexpr int kTPF = kVecOff + 2 * 256;                // + 256 fp32
+constexpr int kQKF = 32 * kFrag;
+constexpr int kKOff = 16 * kFrag;                      // k^ fragments inside a q/k block
+constexpr int kVecOff = 6 * kFrag;
+constexpr int kPOff = kVecOff + 512;                   // after 256 fp32
+constexpr int kTPF = kPOff + 6 * kFrag;
 
 __host__ __device__ constexpr int kpos(int m) { return m < 4 ? 8 * m : 8 * (m - 4) + 4; }
 
@@ -230,28 +223,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     }
     lds_barrier();
 
-    // ---- 1b. q^, k^ and k^T to the workspace as operand fragments
+    // ---- 1b. q^ and k^ to the workspace as operand fragments
     {
         _Float16 *qkb = a.qkf + (((size_t)b * a.nch + c) * a.Hk + kh) * kQKF;
-        for (int idx = tid; idx < 48 * 64; idx += 256) {
+        for (int idx = tid; idx < 32 * 64; idx += 256) {
             const int f = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
-            half8 v;
-            if (f < 32) {
-                const _Float16 *M = f < 16 ? sQ : sK;
-                const int ff = f & 15;
-                const _Float16 *src = M + (16 * (ff >> 2) + fl) * P128 + 32 * (ff & 3) + 4 * fq;
-                const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
-                v = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            } else {
-                const int ff = f - 32;
-                const int key = 16 * (ff >> 1) + fl, tok = 32 * (ff & 1) + 4 * fq;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v[j] = sK[(tok + j) * P128 + key];
-                    v[4 + j] = sK[(tok + 16 + j) * P128 + key];
-                }
-            }
-            *reinterpret_cast<half8 *>(qkb + (size_t)idx * 8) = v;
+            const _Float16 *M = f < 16 ? sQ : sK;
+            const int ff = f & 15;
+            const _Float16 *src = M + (16 * (ff >> 2) + fl) * P128 + 32 * (ff & 3) + 4 * fq;
+            const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
+            *reinterpret_cast<half8 *>(qkb + (size_t)idx * 8) = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
     }
 
@@ -409,7 +390,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }
-            *reinterpret_cast<half8 *>(tpb + (size_t)idx * 8) = v;
+            *reinterpret_cast<half8 *>(tpb + (f < 6 ? 0 : kPOff - 6 * kFrag) + (size_t)idx * 8) = v;
         }
         lds_barrier();
     }
@@ -418,6 +399,23 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
 // ========================================================================
 // chain_kernel<NT>
 // ========================================================================
+
+// Pipeline of one iteration c of the chain workgroup (every role runs iterations
+// 0..nch+2+kLag with one LDS barrier each; the lags keep every hand-off one
+// barrier or more away):
+//   A (state)  chunk c:     X, Delta, S update; Sb(c), Db(c) -> LDS
+//   B (output) chunk c-1:   O = e^G Q S + P Delta -> sO
+//   L (loads)  DMA of the operands of chunk c+2, raw v of chunk c+3 and z of chunk
+//              c-1-kLag; a DMA issued in iteration c is complete at the barrier that
+//              ends iteration c+1, so its data is used from iteration c+2 on
+//   V (VALU)   conv + SiLU of v for chunk c+1; gated RMSNorm and store of chunk
+//              c-3-kLag; the first V wave also publishes the row sums of chunk
+//              c-2 and finishes 1/rms of chunk c-2-kLag from the siblings' sums
+constexpr int kLag = 2;
+constexpr int kRing = 8;           // mailbox slots: chunks c-2-kLag .. c+kLag-2 can be live
+constexpr int kORing = kLag + 3;   // pre-norm output tiles in LDS
+constexpr int kDma = 3;            // operand slots: chunk c+2 loads while chunk c is used
+static_assert(kRing >= 2 * kLag + 1, "mailbox depth");
 
 struct ChainArgs {
     const _Float16 *qkf, *tpf;
@@ -434,103 +432,130 @@ struct ChainArgs {
     float eps_norm;
 };
 
+constexpr int kOpSlot = 16 * 1024;         // operand slot: the chunk's k^ fragments
+constexpr int kSD = 6 * 1024;              // per tile: Sb (4 fragments) and Db (2 fragments)
+
 template <int NT>
 struct ChainLds {
     static constexpr int BV = 16 * NT;
-    static constexpr int VT = BV * PL;                       // floats of one column-major [BV][64] tile
-    static constexpr size_t sV = 0;                           // fp32 [2][BV][PL]      conv(v) of the slice
-    static constexpr size_t sO = sV + 4 * 2 * VT;             // fp32 [kORing][BV][PL] pre-norm output
-    static constexpr size_t sRawV = sO + 4 * kORing * VT;     // bf16 [2][64][BV]      raw v of the slice
-    static constexpr size_t sZ = sRawV + 2 * 2 * kC * BV;     // bf16 [2][64][BV]      z of the slice
-    static constexpr size_t sRstd = sZ + 2 * 2 * kC * BV;     // fp32 [2][64]          gated-norm 1/rms per row
-    static constexpr size_t sCW = sRstd + 4 * 2 * kC;         // fp32 [BV][4]          conv taps of the v channels
-    static constexpr size_t sNW = sCW + 4 * 4 * BV;           // fp32 [BV]             gated-norm weights
+    static constexpr int VT = BV * PL;                          // floats of one column-major [BV][64] tile
+    static constexpr size_t sOp = 0;                             // [kDma][kOpSlot]       DMA'd operands
+    static constexpr size_t sSD = sOp + (size_t)kDma * kOpSlot;  // [2][NT][kSD]         Sb, Db fragments per tile
+    static constexpr size_t sV = sSD + 2 * NT * kSD;             // fp32 [2][BV][PL]      conv(v) of the slice
+    static constexpr size_t sO = sV + 4 * 2 * VT;                // fp32 [kORing][BV][PL] pre-norm output
+    static constexpr size_t sRawV = sO + 4 * kORing * VT;        // bf16 [3][64][BV]      raw v
+    static constexpr size_t sZ = sRawV + 2 * 3 * kC * BV;        // bf16 [3][64][BV]      z
+    static constexpr size_t sHalo = sZ + 2 * 3 * kC * BV;        // bf16 [2][3][BV]       raw v rows before a chunk
+    static constexpr size_t sRstd = sHalo + 2 * 2 * 3 * BV;      // fp32 [2][64]          gated-norm 1/rms
+    static constexpr size_t sCW = sRstd + 4 * 2 * kC;            // fp32 [BV][4]          conv taps of the v channels
+    static constexpr size_t sNW = sCW + 4 * 4 * BV;              // fp32 [BV]             gated-norm weights
     static constexpr size_t bytes = sNW + 4 * BV;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// Operand registers of one chain wave: the fragments of the chunk being
-// computed.  Each set is overwritten with the next chunk's fragments right
-// after its last use in the current chunk.
-struct ChainFrags {
-    half8 k[16], q[16], kt[16], tb[6], p[6];
-    float4 egx[4], ego[4], egc[4];  // e^{G} (for X and for O), e^{G_C - G}: rows 16 I + 4 lq .. +3
-    float dC;                       // e^{G_C}
-};
+#define GDN_AS1 __attribute__((address_space(1)))
+#define GDN_AS3 __attribute__((address_space(3)))
 
-__device__ __forceinline__ void frags_load(ChainFrags &fr, const _Float16 *qkb, const _Float16 *tpb, int lane,
-                                           int lq) {
-    const half8 *qn = reinterpret_cast<const half8 *>(qkb) + lane;
-    const half8 *tn = reinterpret_cast<const half8 *>(tpb) + lane;
-    const float4 *vn = reinterpret_cast<const float4 *>(tpb + kVecOff);
-#pragma unroll
-    for (int f = 0; f < 16; ++f) {
-        fr.q[f] = qn[f * 64];
-        fr.k[f] = qn[(16 + f) * 64];
-        fr.kt[f] = qn[(32 + f) * 64];
-    }
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-        fr.tb[f] = tn[f * 64];
-        fr.p[f] = tn[(6 + f) * 64];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        fr.egx[u] = vn[4 * u + lq];
-        fr.ego[u] = vn[4 * u + lq];
-        fr.egc[u] = vn[16 + 4 * u + lq];
-    }
-    fr.dC = reinterpret_cast<const float *>(tpb + kVecOff)[2 * kC];
+// 16 bytes per lane from global memory (lane address) into LDS at dst + 16 lane
+__device__ __forceinline__ void dma16(const void *src_lane, void *dst_wave) {
+    __builtin_amdgcn_global_load_lds((const GDN_AS1 void *)src_lane, (GDN_AS3 void *)dst_wave, 16, 0, 0);
+}
+// the same through a buffer resource: lanes past the resource read as zero
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, void *dst_wave) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GDN_AS3 void *)dst_wave, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ half8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int f) {
+    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, f * 1024, 0));
+}
+__device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const floatx4 v = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// 4 fp16 from LDS through the transposing read: within each 16-lane group the
+// lanes' 8-byte chunks form a 4 x 16 matrix (row = lane / 4, column = 4 (lane % 4)
+// + element) and lane i receives column i.
+__device__ __forceinline__ half4 lds_tr16(const _Float16 *p) {
+    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s;
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDN_AS3 v4s *)(p));
+    return __builtin_bit_cast(half4, r);
 }
 
-// One chunk of the state chain for one 16-column tile (a chain wave):
-//   X = V - e^G (K S);  Delta = T diag(beta) X;  O = e^G (Q S) + P Delta (to sOc);
-//   S = e^{G_C} S + K^T (e^{G_C - G} Delta).
-// S holds the tile in the accumulator layout (key-row tiles ti = 0..7).  qkn /
-// tpn are the next chunk's blocks: each fragment set is reloaded from them
-// after its last use here.  Scheduling barriers keep each phase's MFMAs
-// ahead of the reloads that overwrite their operands.
-__device__ __forceinline__ void chain_step(ChainFrags &fr, floatx4 (&S)[8], const _Float16 *qkn,
-                                           const _Float16 *tpn, const float *sVc, float *sOc, int lane, int jc,
-                                           int lq) {
-    const half8 *qn = reinterpret_cast<const half8 *>(qkn) + lane;
-    const half8 *tn = reinterpret_cast<const half8 *>(tpn) + lane;
-    const float4 *vn = reinterpret_cast<const float4 *>(tpn + kVecOff);
+// Operands of one chunk that the state wave keeps in registers (loaded one
+// chunk ahead): T diag(beta) fragments and the decay vectors.
+struct StateFrags {
+    half8 tb[6];
+    float4 eg[4], egc[4];  // e^{G}, e^{G_C - G}: rows 16 I + 4 lq .. +3
+    float dC;              // e^{G_C}
+};
 
+__device__ __forceinline__ void state_load(StateFrags &fr, const _Float16 *tpb, int lane, int lq) {
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(tpb, kTPF * 2);
+#pragma unroll
+    for (int f = 0; f < 6; ++f) fr.tb[f] = ld_frag(rt, lane * 16, f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        fr.eg[u] = ld_f4(rt, kVecOff * 2 + lq * 16, 64 * u);
+        fr.egc[u] = ld_f4(rt, kVecOff * 2 + lq * 16, 256 + 64 * u);
+    }
+    fr.dC = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rt, 0, kVecOff * 2 + 4 * 2 * kC, 0));
+}
+
+// One chunk of the state chain for one 16-column tile (an A wave):
+// X = V - e^G (K S); Delta = T diag(beta) X; S = e^{G_C} S + K^T (e^{G_C - G} Delta).
+// S holds the tile in the accumulator layout (key-row tiles ti = 0..7); k^
+// fragments come from LDS (k^T through the transposing read); Sb (S before the
+// chunk) and Db (Delta) go to LDS for the output wave of the tile.  fr is
+// reloaded with the next chunk's (tpn) operands after its last use.
+template <int NT>
+__device__ __forceinline__ void state_step(unsigned char *smem, floatx4 (&S)[8], StateFrags &fr,
+                                           const _Float16 *tpn, int c, int t, int lane, int jc, int lq, int trofs) {
+    using L = ChainLds<NT>;
+    const unsigned char *op = smem + L::sOp + (c % kDma) * kOpSlot;
+    const _Float16 *opk = reinterpret_cast<const _Float16 *>(op);
+    const float *sVc = reinterpret_cast<const float *>(smem + L::sV) + (c & 1) * L::VT;
+    half8 *sd = reinterpret_cast<half8 *>(smem + L::sSD + ((c & 1) * NT + t) * kSD) + lane;
+
+    half8 fk[16];
+#pragma unroll
+    for (int f = 0; f < 16; ++f) fk[f] = *reinterpret_cast<const half8 *>(op + f * 1024 + lane * 16);
     float4 vv[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) vv[I] = *reinterpret_cast<const float4 *>(sVc + jc * PL + 16 * I + 4 * lq);
     half8 Sb[4];
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = pack_tiles(S[2 * s2], S[2 * s2 + 1]);
+    for (int s2 = 0; s2 < 4; ++s2) {
+        Sb[s2] = pack_tiles(S[2 * s2], S[2 * s2 + 1]);
+        sd[64 * s2] = Sb[s2];
+    }
     __builtin_amdgcn_sched_barrier(0);
 
-    // K S (token-row tiles I, contraction over keys; k-step outermost: four chains in flight)
+    // K S (k-step outermost: four accumulation chains in flight), X = V - e^G K S
     floatx4 ks[4] = {};
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-        for (int I = 0; I < 4; ++I) ks[I] = mfma16x16x32(fr.k[4 * I + s2], Sb[s2], ks[I]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int f = 0; f < 16; ++f) fr.k[f] = qn[(16 + f) * 64];
-
-    // X = V - e^G K S
+        for (int I = 0; I < 4; ++I) ks[I] = mfma16x16x32(fk[4 * I + s2], Sb[s2], ks[I]);
     floatx4 X[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        X[I][0] = vv[I].x - fr.egx[I].x * ks[I][0];
-        X[I][1] = vv[I].y - fr.egx[I].y * ks[I][1];
-        X[I][2] = vv[I].z - fr.egx[I].z * ks[I][2];
-        X[I][3] = vv[I].w - fr.egx[I].w * ks[I][3];
+        X[I][0] = vv[I].x - fr.eg[I].x * ks[I][0];
+        X[I][1] = vv[I].y - fr.eg[I].y * ks[I][1];
+        X[I][2] = vv[I].z - fr.eg[I].z * ks[I][2];
+        X[I][3] = vv[I].w - fr.eg[I].w * ks[I][3];
     }
     const half8 Xb[2] = {pack_tiles(X[0], X[1]), pack_tiles(X[2], X[3])};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) fr.egx[u] = vn[4 * u + lq];
-    __builtin_amdgcn_sched_barrier(0);
 
     // Delta = T diag(beta) X  (lower triangular: 32-row block s2 uses k-steps <= s2)
-    half8 Db[2], Dsb[2];
+    half8 Dsb[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
         floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
@@ -543,37 +568,69 @@ __device__ __forceinline__ void chain_step(ChainFrags &fr, floatx4 (&S)[8], cons
             d1 = mfma16x16x32(fr.tb[4], Xb[0], d1);
             d1 = mfma16x16x32(fr.tb[5], Xb[1], d1);
         }
-        Db[s2] = pack_tiles(d0, d1);
+        sd[64 * (4 + s2)] = pack_tiles(d0, d1);
         const float4 c0 = fr.egc[2 * s2], c1 = fr.egc[2 * s2 + 1];
         Dsb[s2] = half8{(_Float16)(d0[0] * c0.x), (_Float16)(d0[1] * c0.y), (_Float16)(d0[2] * c0.z),
                         (_Float16)(d0[3] * c0.w), (_Float16)(d1[0] * c1.x), (_Float16)(d1[1] * c1.y),
                         (_Float16)(d1[2] * c1.z), (_Float16)(d1[3] * c1.w)};
     }
-    // the decay of the old state, ahead of the update at the end
 #pragma unroll
     for (int ti = 0; ti < 8; ++ti) S[ti] = S[ti] * fr.dC;
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int f = 0; f < 6; ++f) fr.tb[f] = tn[f * 64];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) fr.egc[u] = vn[16 + 4 * u + lq];
-    fr.dC = reinterpret_cast<const float *>(tpn + kVecOff)[2 * kC];
+    state_load(fr, tpn, lane, lq);
 
-    // Q S
+    // S += K^T Delta~: k^T fragments from the k^ fragments through the transposing read
+    // (tokens 32 s2 + {4 lq + j}: k^ fragment 8 s2 + (ti >> 1); tokens +16: 4 fragments on;
+    // the keys of tile ti are the 8-byte half (ti & 1) of each lane's 16 bytes)
+#pragma unroll
+    for (int ti = 0; ti < 8; ++ti) {
+        floatx4 acc = S[ti];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const _Float16 *base = opk + (8 * s2 + (ti >> 1)) * kFrag + 4 * (ti & 1) + trofs;
+            const half4 lo = lds_tr16(base), hi = lds_tr16(base + 4 * kFrag);
+            acc = mfma16x16x32(half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, Dsb[s2], acc);
+        }
+        S[ti] = acc;
+    }
+}
+
+// Read-out of one chunk for one 16-column tile (a B wave): O = e^G (Q S) + P Delta
+// with Sb, Db from the A wave of the tile; O to LDS (column-major).
+struct OutFrags {
+    half8 q[16], p[6];
+    float4 eg[4];
+};
+
+__device__ __forceinline__ void out_load(OutFrags &fr, const _Float16 *qkb, const _Float16 *tpb, int lane, int lq) {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qkb, kQKF * 2), rt = make_rsrc(tpb, kTPF * 2);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) fr.q[f] = ld_frag(rq, lane * 16, f);
+#pragma unroll
+    for (int f = 0; f < 6; ++f) fr.p[f] = ld_frag(rt, kPOff * 2 + lane * 16, f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fr.eg[u] = ld_f4(rt, kVecOff * 2 + lq * 16, 64 * u);
+}
+
+template <int NT>
+__device__ __forceinline__ void out_step(unsigned char *smem, const OutFrags &fr, int c, int t, int lane, int jc,
+                                         int lq) {
+    using L = ChainLds<NT>;
+    const half8 *sd = reinterpret_cast<const half8 *>(smem + L::sSD + ((c & 1) * NT + t) * kSD) + lane;
+    float *sOc = reinterpret_cast<float *>(smem + L::sO) + (c % kORing) * L::VT;
+    half8 Sb[4], Db[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) Sb[s2] = sd[64 * s2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) Db[s2] = sd[64 * (4 + s2)];
     floatx4 qs[4] = {};
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
         for (int I = 0; I < 4; ++I) qs[I] = mfma16x16x32(fr.q[4 * I + s2], Sb[s2], qs[I]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int f = 0; f < 16; ++f) fr.q[f] = qn[f * 64];
-
-    // O = e^G Q S + P Delta, to LDS (column-major: four consecutive rows per lane)
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        floatx4 ot = {qs[I][0] * fr.ego[I].x, qs[I][1] * fr.ego[I].y, qs[I][2] * fr.ego[I].z,
-                      qs[I][3] * fr.ego[I].w};
+        floatx4 ot = {qs[I][0] * fr.eg[I].x, qs[I][1] * fr.eg[I].y, qs[I][2] * fr.eg[I].z, qs[I][3] * fr.eg[I].w};
         if (I < 2) {
             ot = mfma16x16x32(fr.p[I], Db[0], ot);
         } else {
@@ -582,23 +639,6 @@ __device__ __forceinline__ void chain_step(ChainFrags &fr, floatx4 (&S)[8], cons
         }
         *reinterpret_cast<float4 *>(sOc + jc * PL + 16 * I + 4 * lq) = make_float4(ot[0], ot[1], ot[2], ot[3]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int f = 0; f < 6; ++f) fr.p[f] = tn[(6 + f) * 64];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) fr.ego[u] = vn[4 * u + lq];
-
-    // S += K^T Delta~  (key-row tiles ti, contraction over tokens)
-#pragma unroll
-    for (int ti = 0; ti < 8; ++ti) {
-        floatx4 acc = S[ti];
-        acc = mfma16x16x32(fr.kt[2 * ti], Dsb[0], acc);
-        acc = mfma16x16x32(fr.kt[2 * ti + 1], Dsb[1], acc);
-        S[ti] = acc;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int f = 0; f < 16; ++f) fr.kt[f] = qn[(32 + f) * 64];
 }
 
 __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, uint32_t tag, unsigned int *err,
@@ -620,28 +660,23 @@ __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, u
     return w;
 }
 
-// Raw v (of one chunk) and z (of another) for the slice, in registers: piece
-// i = lane + 64 u is row i / NCG, 8 columns at 8 (i % NCG).
-template <int NT>
-struct VZStage {
-    static constexpr int NCG = 2 * NT;  // 8-column groups per row
-    static constexpr int N = NCG;       // pieces per lane: 64 rows * NCG / 64
-    u32x4 v[N], z[N];
-};
+__device__ __forceinline__ int mod3(int x) { return ((x % 3) + 3) % 3; }
 
 template <int NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chain_kernel(ChainArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void chain_kernel(ChainArgs a) {
     using L = ChainLds<NT>;
-    using ST = VZStage<NT>;
     constexpr int BV = L::BV, VT = L::VT;
     constexpr int NSL = kTiles / NT;
-    constexpr int NCG = ST::NCG;
-    constexpr int NG = 3 - NT;  // gate waves
+    constexpr int NCG = BV / 8;                 // 8-column groups per slice row
+    constexpr int NV = 8 - 2 * NT - 1;          // VALU helper waves
+    constexpr int NRD = kC * BV * 2 / 1024;     // DMA instructions for 64 rows of raw v (or z) of the slice
+    constexpr int GROUP = kOpSlot / 1024 + 2 * NRD;  // DMA instructions the load wave issues per iteration
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float *sV = reinterpret_cast<float *>(smem + L::sV);
     float *sO = reinterpret_cast<float *>(smem + L::sO);
     uint16_t *sRawV = reinterpret_cast<uint16_t *>(smem + L::sRawV);
     uint16_t *sZ = reinterpret_cast<uint16_t *>(smem + L::sZ);
+    uint16_t *sHalo = reinterpret_cast<uint16_t *>(smem + L::sHalo);
     float *sRstd = reinterpret_cast<float *>(smem + L::sRstd);
     float *sCW = reinterpret_cast<float *>(smem + L::sCW);
     float *sNW = reinterpret_cast<float *>(smem + L::sNW);
@@ -649,10 +684,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches are scalar
     const int l16 = lane & 15, lq = lane >> 4;
-    // roles: waves 0..NT-1 chain; wave NT loads raw v / z, converts v and runs the
-    // norm exchange; the remaining waves apply the gated norm and store o
-    const bool is_chain = wave < NT, is_lm = wave == NT;
-    const int gtid = tid - 64 * (NT + 1);  // gate-thread index (valid on gate waves)
+    const bool is_a = wave < NT, is_b = wave >= NT && wave < 2 * NT, is_l = wave == 2 * NT;
+    const int vh = wave - 2 * NT - 1;  // VALU-helper index (valid when >= 0)
     int broken = 0;
     __shared__ int s_item;
     // Work items (chain, slice) come from eight queues, one per XCD: chain c
@@ -673,10 +706,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (; qi < 8 && item < 0; ) {
                 const int q = (xcc + qi) & 7;
                 const int nq = n_chains > q ? (n_chains - q + 7) / 8 : 0;
-                const unsigned int t = __hip_atomic_fetch_add(a.tickets + q, 1u, __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT);
-                if (t < (unsigned int)(nq * NSL))
-                    item = (q + 8 * (int)(t / NSL)) * NSL + (int)(t % NSL);
+                const unsigned int tk = __hip_atomic_fetch_add(a.tickets + q, 1u, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+                if (tk < (unsigned int)(nq * NSL))
+                    item = (q + 8 * (int)(tk / NSL)) * NSL + (int)(tk % NSL);
                 else
                     ++qi;
             }
@@ -689,24 +722,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int chain = item / NSL, s = item % NSL;
         const int b = chain / a.Hv, h = chain % a.Hv, kh = h / a.r;
         const int sv0 = s * BV;
-        const int last = a.nch + kLag;  // iterations 0..last: chunk c, norm of c-kLag, store of c-kLag-1
+        const int last = a.nch + 2 + kLag;
+        const size_t qk_stride = (size_t)a.Hk * kQKF, tp_stride = (size_t)a.Hv * kTPF;
+        const _Float16 *qk0 = a.qkf + ((size_t)b * a.nch * a.Hk + kh) * kQKF;
+        const _Float16 *tp0 = a.tpf + ((size_t)b * a.nch * a.Hv + h) * kTPF;
 
-        // weights of the slice
-        if (tid >= 64 * NT && tid < 64 * NT + BV) {
-            const int j = tid - 64 * NT, chn = 2 * a.Hk * kD + h * kD + sv0 + j;
-#pragma unroll
-            for (int t4 = 0; t4 < 4; ++t4) sCW[j * 4 + t4] = a.conv ? bf16_to_f32(a.conv_w[(size_t)chn * 4 + t4]) : 0.0f;
-            sNW[j] = a.norm ? bf16_to_f32(a.norm_w[sv0 + j]) : 1.0f;
-        }
-        lds_barrier();
-
-        if (is_chain) {
-            const int jc = 16 * wave + l16;  // column of this lane inside the slice
-            const size_t qk_stride = (size_t)a.Hk * kQKF, tp_stride = (size_t)a.Hv * kTPF;
-            const _Float16 *qk0 = a.qkf + ((size_t)b * a.nch * a.Hk + kh) * kQKF;
-            const _Float16 *tp0 = a.tpf + ((size_t)b * a.nch * a.Hv + h) * kTPF;
-            ChainFrags fr;
-            frags_load(fr, qk0, tp0, lane, lq);
+        if (is_a) {
+            // ---------------------------------------------------------- state wave
+            const int jc = 16 * wave + l16;
+            // transposing-read lane offset (fp16 elements): row j = l16 / 4 of the 16-lane
+            // group, 4-key chunk q = l16 % 4 -> k^ fragment lane (4 lq + j) + 16 q
+            const int trofs = ((4 * lq + (l16 >> 2)) + 16 * (l16 & 3)) * 8;
+            StateFrags fr;
+            state_load(fr, tp0, lane, lq);
             floatx4 S[8];
             {
                 const float *src = a.state_in ? a.state_in + (size_t)chain * kD * kD : nullptr;
@@ -716,13 +744,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     for (int e = 0; e < 4; ++e)
                         S[ti][e] = src ? src[(size_t)(16 * ti + 4 * lq + e) * kD + sv0 + jc] : 0.0f;
             }
-            lds_barrier();  // (prologue: v of chunk 0 converted)
+            lds_barrier();
+            lds_barrier();
             for (int c = 0; c <= last; ++c) {
-                if (c < a.nch) {
-                    const int cn = c + 1 < a.nch ? c + 1 : c;  // (the last chunk re-reads its own blocks)
-                    chain_step(fr, S, qk0 + cn * qk_stride, tp0 + cn * tp_stride, sV + (c & 1) * VT,
-                               sO + (c % kORing) * VT, lane, jc, lq);
-                }
+                if (c < a.nch)
+                    state_step<NT>(smem, S, fr, tp0 + min(c + 1, a.nch - 1) * tp_stride, c, wave, lane, jc, lq, trofs);
                 lds_barrier();
             }
 #pragma unroll
@@ -730,121 +756,211 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     a.state_out[(size_t)chain * kD * kD + (size_t)(16 * ti + 4 * lq + e) * kD + sv0 + jc] = S[ti][e];
-        } else if (is_lm) {
-            const uint16_t *zsrc = a.norm ? a.z : a.v;
-            // issue the loads of raw v rows of chunk cv and z rows of chunk cz (rows are clamped to
-            // valid tokens here and zeroed when stored, so issuing never waits for a load)
-            auto stage_issue = [&](ST &st, int cv, int cz) __attribute__((always_inline)) {
+        } else if (is_b) {
+            // ---------------------------------------------------------- output wave
+            const int t = wave - NT, jc = 16 * t + l16;
+            OutFrags fr;
+            out_load(fr, qk0, tp0, lane, lq);
+            lds_barrier();
+            lds_barrier();
+            for (int c = 0; c <= last; ++c) {
+                if (c >= 1 && c - 1 < a.nch) {
+                    out_step<NT>(smem, fr, c - 1, t, lane, jc, lq);
+                    if (c < a.nch) out_load(fr, qk0 + c * qk_stride, tp0 + c * tp_stride, lane, lq);
+                }
+                lds_barrier();
+            }
+        } else if (is_l) {
+            // ---------------------------------------------------------- load wave (DMA only)
+            // raw v / z rows of chunk cc: a buffer from the chunk's first token, so rows past T read as 0;
+            // lane -> row (64 / NRD rows per instruction), 8-column group
+            auto rows_dma = [&](const uint16_t *x, int cc, uint16_t *dst) __attribute__((always_inline)) {
+                const int c0 = min(max(cc, 0), a.nch - 1) * kC;
+                const unsigned int nrow = (unsigned int)min(a.T - c0, kC);
+                const __amdgpu_buffer_rsrc_t r =
+                    make_rsrc(x + ((size_t)b * a.T + c0) * a.Hv * kD, nrow * (unsigned int)a.Hv * kD * 2);
 #pragma unroll
-                for (int u = 0; u < ST::N; ++u) {
+                for (int u = 0; u < NRD; ++u) {
                     const int i = lane + 64 * u, row = i / NCG, cg = i % NCG;
-                    const int tv = min(max(cv, 0) * kC + row, a.T - 1), tz = min(max(cz, 0) * kC + row, a.T - 1);
-                    st.v[u] = *reinterpret_cast<const u32x4 *>(a.v + (((size_t)b * a.T + tv) * a.Hv + h) * kD + sv0 + 8 * cg);
-                    st.z[u] = *reinterpret_cast<const u32x4 *>(zsrc + (((size_t)b * a.T + tz) * a.Hv + h) * kD + sv0 + 8 * cg);
+                    dma16b(r, ((row * a.Hv + h) * kD + sv0 + 8 * cg) * 2, dst + u * 512);
                 }
             };
-            auto stage_store = [&](const ST &st, int cv, int cz) __attribute__((always_inline)) {
-                u32x4 *dv = reinterpret_cast<u32x4 *>(sRawV + (cv & 1) * kC * BV);
-                u32x4 *dz = reinterpret_cast<u32x4 *>(sZ + (cz & 1) * kC * BV);
+            auto ops_dma = [&](int cc) __attribute__((always_inline)) {
+                const int cl = min(cc, a.nch - 1);  // (past the last chunk: a harmless duplicate)
+                unsigned char *slot = smem + L::sOp + (cc % kDma) * kOpSlot;
+                const _Float16 *kb = qk0 + cl * qk_stride + kKOff;
 #pragma unroll
-                for (int u = 0; u < ST::N; ++u) {
-                    const int i = lane + 64 * u, row = i / NCG;
-                    const bool okv = cv >= 0 && cv * kC + row < a.T, okz = cz >= 0 && cz * kC + row < a.T;
-                    dv[i] = okv ? st.v[u] : u32x4{0u, 0u, 0u, 0u};
-                    dz[i] = okz ? st.z[u] : u32x4{0u, 0u, 0u, 0u};
-                }
+                for (int f = 0; f < 16; ++f) dma16(kb + f * kFrag + lane * 8, slot + f * 1024);
             };
-            // conv + SiLU of the slice of v for chunk cc, from raw rows in LDS, into sV[cc & 1]
+            const uint16_t *zsrc = a.norm ? a.z : a.v;
+            // prologue: operands of chunks 0 and 1, raw v of chunks 0..2
+            ops_dma(0);
+            ops_dma(1);
+            rows_dma(a.v, 0, sRawV);
+            rows_dma(a.v, 1, sRawV + kC * BV);
+            rows_dma(a.v, 2, sRawV + 2 * kC * BV);
+            wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+            for (int c = 0; c <= last; ++c) {
+                // this iteration's group: operands of chunk c+2, raw v of chunk c+3, z of chunk c-1-kLag
+                ops_dma(c + 2);
+                rows_dma(a.v, c + 3, sRawV + mod3(c + 3) * kC * BV);
+                rows_dma(zsrc, c - 1 - kLag, sZ + mod3(c - 1 - kLag) * kC * BV);
+                // the previous iteration's group (chunk c+1) has landed
+                wait_vmcnt<GROUP>();
+                __builtin_amdgcn_s_barrier();
+            }
+            wait_vmcnt<0>();
+        } else {
+            // ---------------------------------------------------------- VALU helpers
+            const int vtid = vh * 64 + lane;
+            if (vtid < BV) {
+                const int chn = 2 * a.Hk * kD + h * kD + sv0 + vtid;
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4)
+                    sCW[vtid * 4 + t4] = a.conv ? bf16_to_f32(a.conv_w[(size_t)chn * 4 + t4]) : 0.0f;
+                sNW[vtid] = a.norm ? bf16_to_f32(a.norm_w[sv0 + vtid]) : 1.0f;
+            }
+            // conv-state rows (or zeros): the three raw rows before chunk 0
+            if (vtid >= 64 && vtid < 64 + 3 * NCG) {
+                const int r3 = (vtid - 64) / NCG, cg = (vtid - 64) % NCG;
+                uint4 rw = make_uint4(0, 0, 0, 0);
+                if (a.conv && a.conv_state_in)
+                    rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + r3) * a.Cc + 2 * a.Hk * kD +
+                                                          h * kD + sv0 + cg * 8);
+                *reinterpret_cast<uint4 *>(sHalo + r3 * BV + cg * 8) = rw;
+            }
+            // A lane always serves the same 8-column group (NV * 64 is a multiple of NCG), so its
+            // conv taps and norm weights live in registers once the prologue has staged them.
+            const int cgl = vtid % NCG;
+            float hw[32], nw[8];
+            // conv + SiLU of v for chunk cc (raw slot cc % 3, the three rows before it from
+            // sHalo[cc & 1]) -> sV[cc & 1]; the chunk's last three rows -> sHalo[(cc + 1) & 1]
             auto conv_v = [&](int cc) __attribute__((always_inline)) {
-                float *dst = sV + (cc & 1) * VT;
-                const uint16_t *cur = sRawV + (cc & 1) * kC * BV;
-                const uint16_t *prev = sRawV + ((cc + 1) & 1) * kC * BV;  // chunk cc-1: its last three rows are the halo
-#pragma unroll
-                for (int u = 0; u < NCG; ++u) {
-                    const int it = lane + 64 * u, row = it / NCG, cg = it % NCG;
-                    float x[4][8];
+                float *dst = sV + (cc & 1) * VT + cgl * 8 * PL;
+                const uint16_t *cur = sRawV + mod3(cc) * kC * BV + cgl * 8;
+                const uint16_t *prev = sHalo + (cc & 1) * 3 * BV + cgl * 8 - (kC - 3) * BV;  // row kC+r2 -> halo row 3+r2
+                if (vtid < 3 * NCG) {
+                    const int r3 = vtid / NCG, cg = vtid % NCG;
+                    *reinterpret_cast<uint4 *>(sHalo + ((cc + 1) & 1) * 3 * BV + r3 * BV + cg * 8) =
+                        *reinterpret_cast<const uint4 *>(sRawV + mod3(cc) * kC * BV + (kC - 3 + r3) * BV + cg * 8);
+                }
+#pragma unroll 1
+                for (int it = vtid; it < kC * NCG; it += NV * 64) {
+                    const int row = it / NCG;
+                    uint4 rw[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int r2 = row - 3 + j;
-                        uint4 rw = make_uint4(0, 0, 0, 0);
-                        if (j == 3 || a.conv) {
-                            if (r2 >= 0)
-                                rw = *reinterpret_cast<const uint4 *>(cur + r2 * BV + cg * 8);
-                            else if (cc > 0)
-                                rw = *reinterpret_cast<const uint4 *>(prev + (kC + r2) * BV + cg * 8);
-                            else if (a.conv_state_in)
-                                rw = *reinterpret_cast<const uint4 *>(
-                                    a.conv_state_in + ((size_t)b * 3 + (3 + r2)) * a.Cc + 2 * a.Hk * kD + h * kD + sv0 + cg * 8);
-                        }
-                        unpack_bf16x8(rw, x[j]);
+                        rw[j] = *reinterpret_cast<const uint4 *>(r2 >= 0 ? cur + r2 * BV : prev + (kC + r2) * BV);
                     }
-                    const float *hw = sCW + cg * 8 * 4;  // [8 channels][4 taps]
+                    __builtin_amdgcn_sched_barrier(0);
+                    float x[4][8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float u8 = a.conv ? silu(hw[4 * e] * x[0][e] + hw[4 * e + 1] * x[1][e] +
-                                                       hw[4 * e + 2] * x[2][e] + hw[4 * e + 3] * x[3][e])
-                                                : x[3][e];
-                        dst[(cg * 8 + e) * PL + row] = u8;
+                    for (int j = 0; j < 4; ++j) unpack_bf16x8(rw[j], x[j]);
+                    float u8[8];
+                    if (a.conv) {
+                        float acc[8], t8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[e] = hw[4 * e] * x[0][e] + hw[4 * e + 1] * x[1][e] + hw[4 * e + 2] * x[2][e] +
+                                     hw[4 * e + 3] * x[3][e];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t8[e] = __builtin_amdgcn_exp2f(acc[e] * -1.4426950408889634f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t8[e] = __builtin_amdgcn_rcpf(1.0f + t8[e]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) u8[e] = acc[e] * t8[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) u8[e] = x[3][e];
                     }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dst[e * PL + row] = u8[e];
+                }
+            };
+            // gated RMSNorm + store of chunk oc
+            auto gate = [&](int oc) __attribute__((always_inline)) {
+                const float *src = sO + (oc % kORing) * VT + cgl * 8 * PL;
+                const float *rs = sRstd + (oc & 1) * kC;
+                const uint16_t *zt = sZ + mod3(oc) * kC * BV + cgl * 8;
+#pragma unroll 1
+                for (int it = vtid; it < kC * NCG; it += NV * 64) {
+                    const int row = it / NCG;
+                    const int tt = oc * kC + row;
+                    float y[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] = src[e * PL + row];
+                    const uint4 zr = *reinterpret_cast<const uint4 *>(zt + row * BV);
+                    const float rstd = rs[row];
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (a.norm) {
+                        float zf[8], t8[8];
+                        unpack_bf16x8(zr, zf);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t8[e] = __builtin_amdgcn_exp2f(zf[e] * -1.4426950408889634f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t8[e] = __builtin_amdgcn_rcpf(1.0f + t8[e]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) y[e] = nw[e] * (y[e] * rstd) * (zf[e] * t8[e]);
+                    }
+                    if (tt < a.T)
+                        *reinterpret_cast<uint4 *>(a.o + (((size_t)b * a.T + tt) * a.Hv + h) * kD + sv0 + cgl * 8) =
+                            pack_bf16x8(y);
                 }
             };
             unsigned long long mbw[NSL];
             unsigned long long *mrow = a.mbox + (size_t)chain * kTiles * kRing * kC + lane;  // row = lane
-            auto lm_iter = [&](int c, ST &st) __attribute__((always_inline)) {
-                // partial sums of chunk c-kLag from every slice: issue now, use at the end
-                const bool want_rstd = a.norm && c >= kLag && c - kLag < a.nch;
+            lds_barrier();
+#pragma unroll
+            for (int e = 0; e < 32; ++e) hw[e] = sCW[cgl * 32 + e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) nw[e] = sNW[cgl * 8 + e];
+            conv_v(0);
+            lds_barrier();
+            for (int c = 0; c <= last; ++c) {
+                const int rc = c - 2 - kLag;  // chunk whose 1/rms is finished here
+                const bool want_rstd = vh == 0 && a.norm && rc >= 0 && rc < a.nch;
                 if (want_rstd) {
 #pragma unroll
                     for (int sib = 0; sib < NSL; ++sib)
-                        mbw[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + ((c - kLag) % kRing)) * kC,
+                        mbw[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + (rc % kRing)) * kC,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                // raw v of chunk c+1 and z of chunk c-kLag (loaded two iterations ago) to LDS,
-                // then the loads for two iterations ahead into the same registers
-                stage_store(st, c + 1, c - kLag);
-                stage_issue(st, c + 3, c + 2 - kLag);
                 if (c + 1 < a.nch) conv_v(c + 1);
-                // row sums of chunk c-1 over this slice's columns -> mailbox
-                if (a.norm && c >= 1 && c - 1 < a.nch) {
-                    const float *src = sO + ((c - 1) % kORing) * VT + lane;
+                // row sums of chunk c-2 over this slice's columns -> mailbox (tag c-1)
+                if (vh == 0 && a.norm && c >= 2 && c - 2 < a.nch) {
+                    const float *src = sO + ((c - 2) % kORing) * VT + lane;
+                    float ov[BV];
+#pragma unroll
+                    for (int j = 0; j < BV; ++j) ov[j] = src[j * PL];
+                    __builtin_amdgcn_sched_barrier(0);
                     float ss = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < BV; ++j) ss += src[j * PL] * src[j * PL];
-                    unsigned long long *mb = a.mbox + (((size_t)chain * kTiles + s) * kRing + ((c - 1) % kRing)) * kC + lane;
-                    __hip_atomic_store(mb, ((unsigned long long)(uint32_t)c << 32) | __float_as_uint(ss),
+                    for (int j = 0; j < BV; ++j) ss += ov[j] * ov[j];
+                    unsigned long long *mb =
+                        a.mbox + (((size_t)chain * kTiles + s) * kRing + ((c - 2) % kRing)) * kC + lane;
+                    __hip_atomic_store(mb, ((unsigned long long)(uint32_t)(c - 1) << 32) | __float_as_uint(ss),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
-                // 1/rms of chunk c-kLag's rows
+                const int oc = c - 3 - kLag;
+                if (oc >= 0 && oc < a.nch) gate(oc);
                 if (want_rstd) {
                     float tot = 0.0f;
 #pragma unroll
                     for (int sib = 0; sib < NSL; ++sib) {
-                        if ((uint32_t)(mbw[sib] >> 32) != (uint32_t)(c - kLag + 1))
-                            mbw[sib] = spin_load(mrow + ((size_t)sib * kRing + ((c - kLag) % kRing)) * kC,
-                                                 (uint32_t)(c - kLag + 1), a.err, broken);
+                        if ((uint32_t)(mbw[sib] >> 32) != (uint32_t)(rc + 1))
+                            mbw[sib] = spin_load(mrow + ((size_t)sib * kRing + (rc % kRing)) * kC, (uint32_t)(rc + 1),
+                                                 a.err, broken);
                         tot += __uint_as_float((uint32_t)mbw[sib]);
                     }
-                    sRstd[((c - kLag) & 1) * kC + lane] = 1.0f / sqrtf(tot * (1.0f / kD) + a.eps_norm);
+                    sRstd[(rc & 1) * kC + lane] = 1.0f / sqrtf(tot * (1.0f / kD) + a.eps_norm);
                 }
-            };
-            // prologue: raw v of chunk 0 -> LDS -> conv; loads of the first two stages
-            ST st0, st1;
-            stage_issue(st0, 0, -1);
-            stage_store(st0, 0, -1);
-            conv_v(0);
-            stage_issue(st0, 1, -kLag);
-            stage_issue(st1, 2, 1 - kLag);
-            lds_barrier();
-            for (int c = 0; c <= last; c += 2) {
-                lm_iter(c, st0);
                 lds_barrier();
-                if (c + 1 <= last) {
-                    lm_iter(c + 1, st1);
-                    lds_barrier();
-                }
             }
             // raw v inputs of the last three tokens -> conv state out
-            if (a.conv && a.conv_state_out && lane < 3 * NCG) {
+            if (vh == 0 && a.conv && a.conv_state_out && lane < 3 * NCG) {
                 const int sidx = lane / NCG, cg = lane % NCG;
                 const int tau = a.T - 3 + sidx;
                 const int ch = 2 * a.Hk * kD + h * kD + sv0 + cg * 8;
@@ -854,36 +970,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 else if (a.conv_state_in)
                     rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + tau)) * a.Cc + ch);
                 *reinterpret_cast<uint4 *>(a.conv_state_out + ((size_t)b * 3 + sidx) * a.Cc + ch) = rw;
-            }
-        } else {
-            // gate waves: gated RMSNorm + store of chunk c-kLag-1
-            lds_barrier();
-            for (int c = 0; c <= last; ++c) {
-                const int oc = c - kLag - 1;
-                if (oc >= 0 && oc < a.nch) {
-                    const float *src = sO + (oc % kORing) * VT;
-                    const float *rs = sRstd + (oc & 1) * kC;
-                    const uint16_t *zt = sZ + (oc & 1) * kC * BV;
-#pragma unroll 1
-                    for (int it = gtid; it < kC * NCG; it += NG * 64) {
-                        const int row = it / NCG, cg = it % NCG;
-                        const int t = oc * kC + row;
-                        if (t >= a.T) continue;
-                        float y[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) y[e] = src[(cg * 8 + e) * PL + row];
-                        if (a.norm) {
-                            float zf[8];
-                            unpack_bf16x8(*reinterpret_cast<const uint4 *>(zt + row * BV + cg * 8), zf);
-                            const float rstd = rs[row];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) y[e] = sNW[cg * 8 + e] * (y[e] * rstd) * silu(zf[e]);
-                        }
-                        *reinterpret_cast<uint4 *>(a.o + (((size_t)b * a.T + t) * a.Hv + h) * kD + sv0 + cg * 8) =
-                            pack_bf16x8(y);
-                    }
-                }
-                lds_barrier();
             }
         }
 
@@ -898,7 +984,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             lds_barrier();
             if (last_one) {
                 unsigned long long *mb = a.mbox + (size_t)chain * kTiles * kRing * kC;
-                for (int i = tid; i < kTiles * kRing * kC; i += 256)
+                for (int i = tid; i < kTiles * kRing * kC; i += 512)
                     __hip_atomic_store(mb + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (tid == 0) __hip_atomic_store(a.counters + chain, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -930,7 +1016,7 @@ int launch_chain(const ChainArgs &base, hipStream_t stream) {
     if ((e = hipGetDevice(&dev)) != hipSuccess) return fail("hipGetDevice", e);
     if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
         return fail("hipDeviceGetAttribute(multiprocessor count)", e);
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn), 256, lds)) !=
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn), 512, lds)) !=
         hipSuccess)
         return fail("hipOccupancyMaxActiveBlocksPerMultiprocessor(chain_kernel)", e);
     constexpr int NSL = kTiles / NT;
@@ -943,7 +1029,7 @@ int launch_chain(const ChainArgs &base, hipStream_t stream) {
     const int grid = a.n_items < cap ? a.n_items : cap;
     a.grid = grid;
     void *args[] = {&a};
-    e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(grid), dim3(256), args, lds, stream);
+    e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(grid), dim3(512), args, lds, stream);
     return e == hipSuccess ? 0 : fail("hipLaunchKernel(chain_kernel)", e);
 }
 
