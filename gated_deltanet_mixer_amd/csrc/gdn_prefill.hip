@@ -123,21 +123,25 @@ struct PrepArgs {
     float eps_l2;
 };
 
+// The q^/k^ tiles are dead once Q K^T and K K^T sit in registers, so the
+// per-value-head buffers overlay them.
 struct PrepLds {
     static constexpr size_t sQ = 0;                        // fp16 [64][P128]
     static constexpr size_t sK = sQ + 2 * kC * P128;       // fp16 [64][P128]
-    static constexpr size_t sL = sK + 2 * kC * P128;       // fp32 [64][PL]
+    static constexpr size_t sL = 0;                        // fp32 [64][PL]    (per value head from here on)
     static constexpr size_t sTd = sL + 4 * kC * PL;        // fp32 [4][16][PTD]
     static constexpr size_t sT16T = sTd + 4 * 4 * 16 * PTD;  // fp16 [64][P64]  T transposed
     static constexpr size_t sPst = sT16T + 2 * kC * P64;   // fp16 [10][256]  P staging
     static constexpr size_t sTbst = sPst + 2 * 10 * kBlk;  // fp16 [10][256]  T diag(beta) staging
     static constexpr size_t sG = sTbst + 2 * 10 * kBlk;    // fp32 [64]
     static constexpr size_t sB = sG + 4 * kC;              // fp32 [64]
-    static constexpr size_t bytes = sB + 4 * kC;
+    static constexpr size_t sGr = sB + 4 * kC;             // fp32 [r][64] g, then [r][64] beta, of every value head
+    static_assert(sGr >= sK + 2 * kC * P128, "g/beta staging must not overlay q^/k^");
+    static size_t bytes(int r) { return sGr + 2 * 4 * (size_t)kC * r; }
 };
 
 // grid (nch, Hk, B), 256 threads
-__global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_prep_kernel(PrepArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + PrepLds::sQ);
     _Float16 *sK = reinterpret_cast<_Float16 *>(smem + PrepLds::sK);
@@ -153,6 +157,21 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
     const int l16 = lane & 15, lq = lane >> 4;
     const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
     const int tc0 = c * kC;
+    float *sGr = reinterpret_cast<float *>(smem + PrepLds::sGr);
+
+    // g and beta of the chunk for the value heads of this key head (zero past T): requested
+    // first, staged in LDS at the end of step 1
+    const int ngb = kC * a.r;
+    float g_ld[2] = {0.f, 0.f}, b_ld[2] = {0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + 256 * u, row = i / a.r, t = tc0 + row;
+        if (i < ngb && t < a.T) {
+            const size_t gi = ((size_t)b * a.T + t) * a.Hv + kh * a.r + i % a.r;
+            g_ld[u] = a.g[gi];
+            b_ld[u] = a.beta[gi];
+        }
+    }
 
     // ---- 1. q/k rows: conv + SiLU + L2 norm.  Thread = (4-token segment, q|k, 8 channels)
     {
@@ -171,20 +190,26 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
             }
         }
         const float qscale = m ? 1.0f : 0.08838834764831845f;  // 1/sqrt(128) on q
+        // both segments' rows are requested before any is used: one memory latency
+        uint4 xr[2][7];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tl0 = ((tid >> 5) + 8 * u) * 4;  // local token of the segment
-            float x[7][8];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int rr = 0; rr < 7; ++rr) {
-                const int t = tc0 + tl0 - 3 + rr;
+                const int t = tc0 + ((tid >> 5) + 8 * u) * 4 - 3 + rr;
                 uint4 raw = make_uint4(0, 0, 0, 0);
                 if (t >= 0 && t < a.T)
                     raw = *reinterpret_cast<const uint4 *>(src + (((size_t)b * a.T + t) * a.Hk + kh) * kD + cg * 8);
                 else if (t < 0 && a.conv && a.conv_state_in)
                     raw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + t)) * a.Cc + ch);
-                unpack_bf16x8(raw, x[rr]);
+                xr[u][rr] = raw;
             }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tl0 = ((tid >> 5) + 8 * u) * 4;  // local token of the segment
+            float x[7][8];
+#pragma unroll
+            for (int rr = 0; rr < 7; ++rr) unpack_bf16x8(xr[u][rr], x[rr]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float uu[8];
@@ -220,6 +245,20 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
                 raw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + tau)) * a.Cc + cc);
             *reinterpret_cast<uint4 *>(a.conv_state_out + ((size_t)b * 3 + s) * a.Cc + cc) = raw;
         }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = tid + 256 * u;
+        if (i < ngb) {
+            sGr[(i % a.r) * kC + i / a.r] = g_ld[u];
+            sGr[(a.r + i % a.r) * kC + i / a.r] = b_ld[u];
+        }
+    }
+    for (int i = tid + 512; i < ngb; i += 256) {  // more than 8 value heads per key head
+        const int row = i / a.r, t = tc0 + row;
+        const size_t gi = ((size_t)b * a.T + t) * a.Hv + kh * a.r + i % a.r;
+        sGr[(i % a.r) * kC + row] = t < a.T ? a.g[gi] : 0.0f;
+        sGr[(a.r + i % a.r) * kC + row] = t < a.T ? a.beta[gi] : 0.0f;
     }
     lds_barrier();
 
@@ -262,11 +301,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(PrepArgs a) {
         const int h = kh * a.r + hr;
         _Float16 *tpb = a.tpf + (((size_t)b * a.nch + c) * a.Hv + h) * kTPF;
         if (wave == 0) {
-            const int t = tc0 + lane;
-            const bool valid = t < a.T;
-            const size_t gi = ((size_t)b * a.T + (valid ? t : 0)) * a.Hv + h;
-            float gv = valid ? a.g[gi] : 0.0f;
-            const float bv = valid ? a.beta[gi] : 0.0f;
+            float gv = sGr[hr * kC + lane];
+            const float bv = sGr[(a.r + hr) * kC + lane];
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
                 const float t2 = __shfl_up(gv, o, 64);
@@ -1069,11 +1105,11 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     pa.Cc = 2 * p.Hk * kD + p.Hv * kD; pa.conv = p.conv_width == 4; pa.nch = plan.nchunks;
     pa.eps_l2 = p.eps_l2;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)PrepLds::bytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)PrepLds::bytes(p.Hv / p.Hk));
     if (e != hipSuccess) return fail("hipFuncSetAttribute(chunk_prep_kernel)", e);
     void *pargs[] = {&pa};
     e = hipLaunchKernel(reinterpret_cast<const void *>(chunk_prep_kernel),
-                        dim3((unsigned)plan.nchunks, (unsigned)p.Hk, (unsigned)p.B), dim3(256), pargs, PrepLds::bytes,
+                        dim3((unsigned)plan.nchunks, (unsigned)p.Hk, (unsigned)p.B), dim3(256), pargs, PrepLds::bytes(p.Hv / p.Hk),
                         stream);
     if (e != hipSuccess) return fail("hipLaunchKernel(chunk_prep_kernel)", e);
 
