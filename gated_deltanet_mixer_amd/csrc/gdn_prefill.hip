@@ -109,6 +109,42 @@ __device__ __forceinline__ half8 pack_tiles(const floatx4 &a, const floatx4 &b) 
                  (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
 }
 
+#define GDN_AS1 __attribute__((address_space(1)))
+#define GDN_AS3 __attribute__((address_space(3)))
+
+// 16 bytes per lane from global memory (lane address) into LDS at dst + 16 lane
+__device__ __forceinline__ void dma16(const void *src_lane, void *dst_wave) {
+    __builtin_amdgcn_global_load_lds((const GDN_AS1 void *)src_lane, (GDN_AS3 void *)dst_wave, 16, 0, 0);
+}
+// the same through a buffer resource: lanes past the resource read as zero
+__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, void *dst_wave) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GDN_AS3 void *)dst_wave, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ half8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int f) {
+    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, f * 1024, 0));
+}
+__device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    const floatx4 v = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// 4 fp16 from LDS through the transposing read: within each 16-lane group the
+// lanes' 8-byte chunks form a 4 x 16 matrix (row = lane / 4, column = 4 (lane % 4)
+// + element) and lane i receives column i.
+__device__ __forceinline__ half4 lds_tr16(const _Float16 *p) {
+    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s;
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDN_AS3 v4s *)(p));
+    return __builtin_bit_cast(half4, r);
+}
+
 // ========================================================================
 // chunk_prep_kernel
 // ========================================================================
@@ -153,7 +189,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     float *sG = reinterpret_cast<float *>(smem + PrepLds::sG);
     float *sB = reinterpret_cast<float *>(smem + PrepLds::sB);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave bases stay scalar
     const int l16 = lane & 15, lq = lane >> 4;
     const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
     const int tc0 = c * kC;
@@ -173,74 +210,97 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
     }
 
-    // ---- 1. q/k rows: conv + SiLU + L2 norm.  Thread = (4-token segment, q|k, 8 channels)
+    // ---- 1. q/k rows: conv + SiLU + L2 norm.  Thread = (q|k by wave parity, two 4-token
+    //         segments, 8 channels)
     {
-        const int cg = tid & 15, m = (tid >> 4) & 1;
-        const uint16_t *src = m ? a.k : a.q;
+        const int cg = lane & 15, m = wave & 1;
+        const int seg0 = (wave >> 1) * 4 + (lane >> 4);  // segments seg0 and seg0 + 8
         const int ch = m * a.Hk * kD + kh * kD + cg * 8;  // conv channel of element 0
-        float w[8][4];
-        if (a.conv) {
-            const uint4 *wp = reinterpret_cast<const uint4 *>(a.conv_w + (size_t)ch * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float tmp[8];
-                unpack_bf16x8(wp[i], tmp);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w[(8 * i + e) >> 2][(8 * i + e) & 3] = tmp[e];
-            }
-        }
-        const float qscale = m ? 1.0f : 0.08838834764831845f;  // 1/sqrt(128) on q
-        // both segments' rows are requested before any is used: one memory latency
+        // rows tc0 - 3 .. tc0 + 63 through one buffer resource from the first row it covers:
+        // rows past T read as zero; rows before the sequence come from the conv state
+        const int r0 = c > 0 ? tc0 - 3 : 0;
+        const unsigned int rowb = (unsigned int)a.Hk * kD * 2;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc((m ? a.k : a.q) + ((size_t)b * a.T + r0) * a.Hk * kD + kh * kD,
+                      (unsigned int)(min(a.T, tc0 + kC) - r0) * rowb);
         uint4 xr[2][7];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int rr = 0; rr < 7; ++rr) {
-                const int t = tc0 + ((tid >> 5) + 8 * u) * 4 - 3 + rr;
-                uint4 raw = make_uint4(0, 0, 0, 0);
-                if (t >= 0 && t < a.T)
-                    raw = *reinterpret_cast<const uint4 *>(src + (((size_t)b * a.T + t) * a.Hk + kh) * kD + cg * 8);
-                else if (t < 0 && a.conv && a.conv_state_in)
-                    raw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + t)) * a.Cc + ch);
-                xr[u][rr] = raw;
+                const int t = tc0 + (seg0 + 8 * u) * 4 - 3 + rr;
+                xr[u][rr] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rs, (int)((t - r0) * (int)rowb) + cg * 16, 0, 0));
             }
+        if (c == 0) {  // the conv-history rows of the first chunk (only segment 0 has any)
+#pragma unroll
+            for (int rr = 0; rr < 3; ++rr) {
+                const int t = seg0 * 4 - 3 + rr;
+                if (t < 0)
+                    xr[0][rr] = (a.conv && a.conv_state_in)
+                                    ? *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + t)) * a.Cc + ch)
+                                    : make_uint4(0, 0, 0, 0);
+            }
+        }
+        uint4 wr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            wr[i] = a.conv ? reinterpret_cast<const uint4 *>(a.conv_w + (size_t)ch * 4)[i] : make_uint4(0, 0, 0, 0);
+        float w[32];  // w[4 e + j]: tap j (row t - 3 + j) of channel e
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float tmp[8];
+            unpack_bf16x8(wr[i], tmp);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[8 * i + e] = tmp[e];
+        }
+        const float qscale = m ? 1.0f : 0.08838834764831845f;  // 1/sqrt(128) on q
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int tl0 = ((tid >> 5) + 8 * u) * 4;  // local token of the segment
+            const int tl0 = (seg0 + 8 * u) * 4;  // local token of the segment
             float x[7][8];
 #pragma unroll
             for (int rr = 0; rr < 7; ++rr) unpack_bf16x8(xr[u][rr], x[rr]);
+            float uu[4][8];
+            if (a.conv) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        uu[i][e] = w[4 * e] * x[i][e] + w[4 * e + 1] * x[i + 1][e] + w[4 * e + 2] * x[i + 2][e] +
+                                   w[4 * e + 3] * x[i + 3][e];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) uu[i][e] = silu(uu[i][e]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) uu[i][e] = x[i + 3][e];
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float uu[8];
                 float ss = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    uu[e] = a.conv ? silu(w[e][0] * x[i][e] + w[e][1] * x[i + 1][e] + w[e][2] * x[i + 2][e] +
-                                          w[e][3] * x[i + 3][e])
-                                   : x[i + 3][e];
-                    ss += uu[e] * uu[e];
-                }
+                for (int e = 0; e < 8; ++e) ss += uu[i][e] * uu[i][e];
                 ss = group_sum<16>(ss);
                 const bool valid = tc0 + tl0 + i < a.T;
                 const float sc = valid ? qscale / sqrtf(ss + a.eps_l2) : 0.0f;  // rows past T are zero
                 half8 hv;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    hv[e] = static_cast<_Float16>(uu[e] * sc);
-                }
-                const int row = tl0 + i;
-                *reinterpret_cast<half8 *>((m ? sK : sQ) + row * P128 + cg * 8) = hv;
+                for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(uu[i][e] * sc);
+                *reinterpret_cast<half8 *>((m ? sK : sQ) + (tl0 + i) * P128 + cg * 8) = hv;
             }
         }
         // raw q/k inputs of the last three tokens -> conv state out
         if (c == 0 && a.conv && a.conv_state_out && tid < 96) {
-            const int s = tid >> 5, mm = (tid >> 4) & 1;
+            const int s = tid >> 5, mm = (tid >> 4) & 1, cq = tid & 15;
             const int tau = a.T - 3 + s;
-            const int cc = mm * a.Hk * kD + kh * kD + cg * 8;
+            const int cc = mm * a.Hk * kD + kh * kD + cq * 8;
             uint4 raw = make_uint4(0, 0, 0, 0);
             if (tau >= 0)
-                raw = *reinterpret_cast<const uint4 *>((mm ? a.k : a.q) + (((size_t)b * a.T + tau) * a.Hk + kh) * kD + cg * 8);
+                raw = *reinterpret_cast<const uint4 *>((mm ? a.k : a.q) + (((size_t)b * a.T + tau) * a.Hk + kh) * kD + cq * 8);
             else if (a.conv_state_in)
                 raw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + tau)) * a.Cc + cc);
             *reinterpret_cast<uint4 *>(a.conv_state_out + ((size_t)b * 3 + s) * a.Cc + cc) = raw;
@@ -488,42 +548,6 @@ struct ChainLds {
     static constexpr size_t bytes = sNW + 4 * BV;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
-
-#define GDN_AS1 __attribute__((address_space(1)))
-#define GDN_AS3 __attribute__((address_space(3)))
-
-// 16 bytes per lane from global memory (lane address) into LDS at dst + 16 lane
-__device__ __forceinline__ void dma16(const void *src_lane, void *dst_wave) {
-    __builtin_amdgcn_global_load_lds((const GDN_AS1 void *)src_lane, (GDN_AS3 void *)dst_wave, 16, 0, 0);
-}
-// the same through a buffer resource: lanes past the resource read as zero
-__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, void *dst_wave) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GDN_AS3 void *)dst_wave, 16, voff, 0, 0, 0);
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ half8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int f) {
-    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, f * 1024, 0));
-}
-__device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    const floatx4 v = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// 4 fp16 from LDS through the transposing read: within each 16-lane group the
-// lanes' 8-byte chunks form a 4 x 16 matrix (row = lane / 4, column = 4 (lane % 4)
-// + element) and lane i receives column i.
-__device__ __forceinline__ half4 lds_tr16(const _Float16 *p) {
-    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s;
-    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDN_AS3 v4s *)(p));
-    return __builtin_bit_cast(half4, r);
-}
 
 // Operands of one chunk that the state wave keeps in registers (loaded one
 // chunk ahead): T diag(beta) fragments and the decay vectors.
