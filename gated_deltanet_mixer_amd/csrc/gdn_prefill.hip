@@ -507,7 +507,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 //   V (VALU)   conv + SiLU of v for chunk c+1; gated RMSNorm and store of chunk
 //              c-3-kLag; the first V wave also publishes the row sums of chunk
 //              c-2 and finishes 1/rms of chunk c-2-kLag from the siblings' sums
-constexpr int kLag = 2;
+constexpr int kLag = 3;
 constexpr int kRing = 8;           // mailbox slots: chunks c-2-kLag .. c+kLag-2 can be live
 constexpr int kORing = kLag + 3;   // pre-norm output tiles in LDS
 constexpr int kDma = 3;            // operand slots: chunk c+2 loads while chunk c is used
@@ -537,8 +537,8 @@ struct ChainLds {
     static constexpr int VT = BV * PL;                          // floats of one column-major [BV][64] tile
     static constexpr size_t sOp = 0;                             // [kDma][kOpSlot]       DMA'd operands
     static constexpr size_t sSD = sOp + (size_t)kDma * kOpSlot;  // [2][NT][kSD]         Sb, Db fragments per tile
-    static constexpr size_t sV = sSD + 2 * NT * kSD;             // fp32 [2][BV][PL]      conv(v) of the slice
-    static constexpr size_t sO = sV + 4 * 2 * VT;                // fp32 [kORing][BV][PL] pre-norm output
+    static constexpr size_t sV = sSD + 2 * NT * kSD;             // fp16 [2][BV][P64]     conv(v) of the slice
+    static constexpr size_t sO = sV + 2 * 2 * BV * P64;          // fp32 [kORing][BV][PL] pre-norm output
     static constexpr size_t sRawV = sO + 4 * kORing * VT;        // bf16 [3][64][BV]      raw v
     static constexpr size_t sZ = sRawV + 2 * 3 * kC * BV;        // bf16 [3][64][BV]      z
     static constexpr size_t sHalo = sZ + 2 * 3 * kC * BV;        // bf16 [2][3][BV]       raw v rows before a chunk
@@ -581,15 +581,15 @@ __device__ __forceinline__ void state_step(unsigned char *smem, floatx4 (&S)[8],
     using L = ChainLds<NT>;
     const unsigned char *op = smem + L::sOp + (c % kDma) * kOpSlot;
     const _Float16 *opk = reinterpret_cast<const _Float16 *>(op);
-    const float *sVc = reinterpret_cast<const float *>(smem + L::sV) + (c & 1) * L::VT;
+    const _Float16 *sVc = reinterpret_cast<const _Float16 *>(smem + L::sV) + (c & 1) * L::BV * P64;
     half8 *sd = reinterpret_cast<half8 *>(smem + L::sSD + ((c & 1) * NT + t) * kSD) + lane;
 
     half8 fk[16];
 #pragma unroll
     for (int f = 0; f < 16; ++f) fk[f] = *reinterpret_cast<const half8 *>(op + f * 1024 + lane * 16);
-    float4 vv[4];
+    half4 vv[4];
 #pragma unroll
-    for (int I = 0; I < 4; ++I) vv[I] = *reinterpret_cast<const float4 *>(sVc + jc * PL + 16 * I + 4 * lq);
+    for (int I = 0; I < 4; ++I) vv[I] = lds_half4(sVc + jc * P64 + 16 * I + 4 * lq);
     half8 Sb[4];
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
@@ -607,10 +607,10 @@ __device__ __forceinline__ void state_step(unsigned char *smem, floatx4 (&S)[8],
     floatx4 X[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        X[I][0] = vv[I].x - fr.eg[I].x * ks[I][0];
-        X[I][1] = vv[I].y - fr.eg[I].y * ks[I][1];
-        X[I][2] = vv[I].z - fr.eg[I].z * ks[I][2];
-        X[I][3] = vv[I].w - fr.eg[I].w * ks[I][3];
+        X[I][0] = (float)vv[I][0] - fr.eg[I].x * ks[I][0];
+        X[I][1] = (float)vv[I][1] - fr.eg[I].y * ks[I][1];
+        X[I][2] = (float)vv[I][2] - fr.eg[I].z * ks[I][2];
+        X[I][3] = (float)vv[I][3] - fr.eg[I].w * ks[I][3];
     }
     const half8 Xb[2] = {pack_tiles(X[0], X[1]), pack_tiles(X[2], X[3])};
 
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NRD = kC * BV * 2 / 1024;     // DMA instructions for 64 rows of raw v (or z) of the slice
     constexpr int GROUP = kOpSlot / 1024 + 2 * NRD;  // DMA instructions the load wave issues per iteration
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float *sV = reinterpret_cast<float *>(smem + L::sV);
+    _Float16 *sV = reinterpret_cast<_Float16 *>(smem + L::sV);
     float *sO = reinterpret_cast<float *>(smem + L::sO);
     uint16_t *sRawV = reinterpret_cast<uint16_t *>(smem + L::sRawV);
     uint16_t *sZ = reinterpret_cast<uint16_t *>(smem + L::sZ);
@@ -898,7 +898,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // conv + SiLU of v for chunk cc (raw slot cc % 3, the three rows before it from
             // sHalo[cc & 1]) -> sV[cc & 1]; the chunk's last three rows -> sHalo[(cc + 1) & 1]
             auto conv_v = [&](int cc) __attribute__((always_inline)) {
-                float *dst = sV + (cc & 1) * VT + cgl * 8 * PL;
+                _Float16 *dst = sV + (cc & 1) * BV * P64 + cgl * 8 * P64;
                 const uint16_t *cur = sRawV + mod3(cc) * kC * BV + cgl * 8;
                 const uint16_t *prev = sHalo + (cc & 1) * 3 * BV + cgl * 8 - (kC - 3) * BV;  // row kC+r2 -> halo row 3+r2
                 if (vtid < 3 * NCG) {
@@ -937,7 +937,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         for (int e = 0; e < 8; ++e) u8[e] = x[3][e];
                     }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) dst[e * PL + row] = u8[e];
+                    for (int e = 0; e < 8; ++e) dst[e * P64 + row] = static_cast<_Float16>(u8[e]);
                 }
             };
             // gated RMSNorm + store of chunk oc
@@ -946,7 +946,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const float *rs = sRstd + (oc & 1) * kC;
                 const uint16_t *zt = sZ + mod3(oc) * kC * BV + cgl * 8;
 #pragma unroll 1
-                for (int it = vtid; it < kC * NCG; it += NV * 64) {
+                for (int it = vtid - 64; it < kC * NCG; it += (NV - 1) * 64) {
                     const int row = it / NCG;
                     const int tt = oc * kC + row;
                     float y[8];
@@ -970,7 +970,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                             pack_bf16x8(y);
                 }
             };
-            unsigned long long mbw[NSL];
             unsigned long long *mrow = a.mbox + (size_t)chain * kTiles * kRing * kC + lane;  // row = lane
             lds_barrier();
 #pragma unroll
@@ -979,45 +978,63 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int e = 0; e < 8; ++e) nw[e] = sNW[cgl * 8 + e];
             conv_v(0);
             lds_barrier();
-            for (int c = 0; c <= last; ++c) {
-                const int rc = c - 2 - kLag;  // chunk whose 1/rms is finished here
-                const bool want_rstd = vh == 0 && a.norm && rc >= 0 && rc < a.nch;
-                if (want_rstd) {
+            // Helper 0 owns the norm's cross-slice exchange and issues no output stores;
+            // the others gate and store.  On this target one counter tracks both loads and
+            // stores, so a wave that waits for a load also waits for every store it issued
+            // before it: keeping the mailbox loads and the output stores in different waves
+            // keeps either from waiting on the other.
+            if (vh == 0) {
+                unsigned long long mbn[NSL] = {};  // sibling words of chunk rc, requested an iteration early
+                auto mb_request = [&](int cc) __attribute__((always_inline)) {
+                    if (a.norm && cc >= 0 && cc < a.nch) {
 #pragma unroll
-                    for (int sib = 0; sib < NSL; ++sib)
-                        mbw[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + (rc % kRing)) * kC,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                if (c + 1 < a.nch) conv_v(c + 1);
-                // row sums of chunk c-2 over this slice's columns -> mailbox (tag c-1)
-                if (vh == 0 && a.norm && c >= 2 && c - 2 < a.nch) {
-                    const float *src = sO + ((c - 2) % kORing) * VT + lane;
-                    float ov[BV];
-#pragma unroll
-                    for (int j = 0; j < BV; ++j) ov[j] = src[j * PL];
-                    __builtin_amdgcn_sched_barrier(0);
-                    float ss = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < BV; ++j) ss += ov[j] * ov[j];
-                    unsigned long long *mb =
-                        a.mbox + (((size_t)chain * kTiles + s) * kRing + ((c - 2) % kRing)) * kC + lane;
-                    __hip_atomic_store(mb, ((unsigned long long)(uint32_t)(c - 1) << 32) | __float_as_uint(ss),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                const int oc = c - 3 - kLag;
-                if (oc >= 0 && oc < a.nch) gate(oc);
-                if (want_rstd) {
-                    float tot = 0.0f;
-#pragma unroll
-                    for (int sib = 0; sib < NSL; ++sib) {
-                        if ((uint32_t)(mbw[sib] >> 32) != (uint32_t)(rc + 1))
-                            mbw[sib] = spin_load(mrow + ((size_t)sib * kRing + (rc % kRing)) * kC, (uint32_t)(rc + 1),
-                                                 a.err, broken);
-                        tot += __uint_as_float((uint32_t)mbw[sib]);
+                        for (int sib = 0; sib < NSL; ++sib)
+                            mbn[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + (cc % kRing)) * kC,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
-                    sRstd[(rc & 1) * kC + lane] = 1.0f / sqrtf(tot * (1.0f / kD) + a.eps_norm);
+                };
+                mb_request(-2 - kLag);
+                for (int c = 0; c <= last; ++c) {
+                    // 1/rms of chunk rc from the siblings' words (published kLag - 1 iterations before
+                    // they were requested; a word without the chunk's tag is waited for)
+                    const int rc = c - 2 - kLag;
+                    if (a.norm && rc >= 0 && rc < a.nch) {
+                        float tot = 0.0f;
+#pragma unroll
+                        for (int sib = 0; sib < NSL; ++sib) {
+                            if ((uint32_t)(mbn[sib] >> 32) != (uint32_t)(rc + 1))
+                                mbn[sib] = spin_load(mrow + ((size_t)sib * kRing + (rc % kRing)) * kC,
+                                                     (uint32_t)(rc + 1), a.err, broken);
+                            tot += __uint_as_float((uint32_t)mbn[sib]);
+                        }
+                        sRstd[(rc & 1) * kC + lane] = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.eps_norm);
+                    }
+                    // row sums of chunk c-2 over this slice's columns -> mailbox (tag c-1)
+                    if (a.norm && c >= 2 && c - 2 < a.nch) {
+                        const float *src = sO + ((c - 2) % kORing) * VT + lane;
+                        float ov[BV];
+#pragma unroll
+                        for (int j = 0; j < BV; ++j) ov[j] = src[j * PL];
+                        __builtin_amdgcn_sched_barrier(0);
+                        float ss = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < BV; ++j) ss += ov[j] * ov[j];
+                        unsigned long long *mb =
+                            a.mbox + (((size_t)chain * kTiles + s) * kRing + ((c - 2) % kRing)) * kC + lane;
+                        __hip_atomic_store(mb, ((unsigned long long)(uint32_t)(c - 1) << 32) | __float_as_uint(ss),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    mb_request(rc + 1);
+                    if (c + 1 < a.nch) conv_v(c + 1);
+                    lds_barrier();
                 }
-                lds_barrier();
+            } else {
+                for (int c = 0; c <= last; ++c) {
+                    if (c + 1 < a.nch) conv_v(c + 1);
+                    const int oc = c - 3 - kLag;
+                    if (oc >= 0 && oc < a.nch) gate(oc);
+                    lds_barrier();
+                }
             }
             // raw v inputs of the last three tokens -> conv state out
             if (vh == 0 && a.conv && a.conv_state_out && lane < 3 * NCG) {
