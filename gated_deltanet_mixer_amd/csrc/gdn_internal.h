@@ -33,6 +33,7 @@ struct PrefillPlan {
     int nchunks;         // ceil(T / 64)
     size_t qk_bytes;     // per (sequence, chunk, key head): q^, k^ [64][128], k^T [128][64] fp16
     size_t tp_bytes;     // per (sequence, chunk, value head): T diag(beta), P (lower blocks, fp16), decay vectors
+    size_t ready_bytes;  // per (sequence, chunk, key head): stamp of the call whose operands are written
     size_t mbox_bytes;   // exchange area (tagged partial sums, counters, error word)
     size_t total_bytes;
 };

@@ -51,6 +51,9 @@
 //                     is bounded.
 // All contractions use fp16 MFMA operands with fp32 accumulation; the state is
 // carried in fp32 across chunks; inputs and outputs are bf16.
+#include <atomic>
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -136,6 +139,19 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Stores of operands that the sequential pass may read while the prep kernel
+// still runs: written through to memory (agent-coherent, the encoding of an
+// agent-scope relaxed atomic store), so a block can publish its stamp after its
+// stores complete without writing back a whole L2.
+constexpr int kWriteThrough = 16;  // sc1
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_through(__amdgpu_buffer_rsrc_t r, int voff, half8 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, kWriteThrough);
+}
+__device__ __forceinline__ void st_through(__amdgpu_buffer_rsrc_t r, int voff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, kWriteThrough);
+}
+
 // 4 fp16 from LDS through the transposing read: within each 16-lane group the
 // lanes' 8-byte chunks form a 4 x 16 matrix (row = lane / 4, column = 4 (lane % 4)
 // + element) and lane i receives column i.
@@ -155,6 +171,8 @@ struct PrepArgs {
     uint16_t *conv_state_out;
     _Float16 *qkf;  // [B][nch][Hk][kQKF]
     _Float16 *tpf;  // [B][nch][Hv][kTPF]
+    unsigned int *ready;  // [B][nch][Hk]: call stamp once the block's operands are written
+    unsigned int stamp;
     int B, T, Hk, Hv, r, Cc, conv, nch;
     float eps_l2;
 };
@@ -176,7 +194,7 @@ struct PrepLds {
     static size_t bytes(int r) { return sGr + 2 * 4 * (size_t)kC * r; }
 };
 
-// grid (nch, Hk, B), 256 threads
+// grid (nch * Hk, B), 256 threads
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_prep_kernel(PrepArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + PrepLds::sQ);
@@ -192,7 +210,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave bases stay scalar
     const int l16 = lane & 15, lq = lane >> 4;
-    const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+    // blocks in chunk-major order, so the sequential pass can start on the first
+    // chunks while later ones are still being prepared
+    const int c = blockIdx.x / a.Hk, kh = blockIdx.x % a.Hk, b = blockIdx.y;
     const int tc0 = c * kC;
     float *sGr = reinterpret_cast<float *>(smem + PrepLds::sGr);
 
@@ -324,14 +344,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
     // ---- 1b. q^ and k^ to the workspace as operand fragments
     {
-        _Float16 *qkb = a.qkf + (((size_t)b * a.nch + c) * a.Hk + kh) * kQKF;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qkf + (((size_t)b * a.nch + c) * a.Hk + kh) * kQKF, kQKF * 2);
         for (int idx = tid; idx < 32 * 64; idx += 256) {
             const int f = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
             const _Float16 *M = f < 16 ? sQ : sK;
             const int ff = f & 15;
             const _Float16 *src = M + (16 * (ff >> 2) + fl) * P128 + 32 * (ff & 3) + 4 * fq;
             const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
-            *reinterpret_cast<half8 *>(qkb + (size_t)idx * 8) = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            st_through(rq, idx * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         }
     }
 
@@ -359,7 +379,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // ---- 3. per value head of this key head
     for (int hr = 0; hr < a.r; ++hr) {
         const int h = kh * a.r + hr;
-        _Float16 *tpb = a.tpf + (((size_t)b * a.nch + c) * a.Hv + h) * kTPF;
+        const __amdgpu_buffer_rsrc_t rtp = make_rsrc(a.tpf + (((size_t)b * a.nch + c) * a.Hv + h) * kTPF, kTPF * 2);
         if (wave == 0) {
             float gv = sGr[hr * kC + lane];
             const float bv = sGr[(a.r + hr) * kC + lane];
@@ -371,10 +391,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const float gc = __shfl(gv, 63, 64);
             sG[lane] = gv;
             sB[lane] = bv;
-            float *vec = reinterpret_cast<float *>(tpb + kVecOff);
-            vec[lane] = __expf(gv);
-            vec[kC + lane] = __expf(gc - gv);
-            if (lane < 4) vec[2 * kC + lane] = __expf(gc);
+            st_through(rtp, kVecOff * 2 + 4 * lane, __expf(gv));
+            st_through(rtp, kVecOff * 2 + 4 * (kC + lane), __expf(gc - gv));
+            if (lane < 4) st_through(rtp, kVecOff * 2 + 4 * (2 * kC + lane), __expf(gc));
         }
         lds_barrier();
 
@@ -486,10 +505,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }
-            *reinterpret_cast<half8 *>(tpb + (f < 6 ? 0 : kPOff - 6 * kFrag) + (size_t)idx * 8) = v;
+            st_through(rtp, ((f < 6 ? 0 : kPOff - 6 * kFrag) + idx * 8) * 2, v);
         }
         lds_barrier();
     }
+    // every wave's (written-through) stores complete, then the block's stamp
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_store(a.ready + ((size_t)b * a.nch + c) * a.Hk + kh, a.stamp, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ========================================================================
@@ -524,6 +549,8 @@ struct ChainArgs {
     unsigned int *err;
     unsigned int *tickets;     // [8] next item of each XCD queue
     unsigned int *exits;       // workgroups that have left the item loop
+    const unsigned int *ready; // [B][nch][Hk] prep stamps
+    unsigned int stamp;
     int B, T, Hk, Hv, r, Cc, conv, norm, nch, n_items, grid;
     float eps_norm;
 };
@@ -722,6 +749,32 @@ __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, u
 
 __device__ __forceinline__ int mod3(int x) { return ((x % 3) + 3) % 3; }
 
+// The prep kernel may still be running while this one starts: prep block
+// (sequence b, chunk cc, key head kh) stores this call's stamp once its operands
+// are written back (agent-scope release).  A chunk's operands are first touched
+// after its stamp has been seen, and no cache of this kernel holds lines of them
+// from before (caches are invalidated when a kernel starts and nothing loads a
+// chunk early), so a relaxed load of the stamp suffices.
+__device__ __forceinline__ const unsigned int *ready_word(const ChainArgs &a, int b, int cc, int kh) {
+    return a.ready + ((size_t)b * a.nch + cc) * a.Hk + kh;
+}
+__device__ __forceinline__ bool stamp_ok(const ChainArgs &a, unsigned int w) { return (int)(w - a.stamp) >= 0; }
+
+// Wait until the prep block is complete.  Bounded like every cross-workgroup
+// wait: on a timeout the error word is raised.
+__device__ __forceinline__ void wait_ready(const ChainArgs &a, int b, int cc, int kh, int &broken) {
+    const unsigned int *f = ready_word(a, b, cc, kh);
+    uint32_t n = 0;
+    while (!stamp_ok(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+        if (broken || ++n > kSpinLimit) {
+            if (!broken) atomicOr(a.err, 1u);
+            broken = 1;
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 template <int NT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void chain_kernel(ChainArgs a) {
     using L = ChainLds<NT>;
@@ -794,6 +847,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // group, 4-key chunk q = l16 % 4 -> k^ fragment lane (4 lq + j) + 16 q
             const int trofs = ((4 * lq + (l16 >> 2)) + 16 * (l16 & 3)) * 8;
             StateFrags fr;
+            wait_ready(a, b, 0, kh, broken);
             state_load(fr, tp0, lane, lq);
             floatx4 S[8];
             {
@@ -820,6 +874,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // ---------------------------------------------------------- output wave
             const int t = wave - NT, jc = 16 * t + l16;
             OutFrags fr;
+            wait_ready(a, b, 0, kh, broken);
             out_load(fr, qk0, tp0, lane, lq);
             lds_barrier();
             lds_barrier();
@@ -853,9 +908,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int f = 0; f < 16; ++f) dma16(kb + f * kFrag + lane * 8, slot + f * 1024);
             };
             const uint16_t *zsrc = a.norm ? a.z : a.v;
-            // prologue: operands of chunks 0 and 1, raw v of chunks 0..2
+            // prologue: operands of chunks 0 and 1, raw v of chunks 0..2.  The load wave is
+            // the one that waits for the prep blocks: A and B load a chunk's operands only
+            // after the barrier that follows its wait.
+            wait_ready(a, b, 0, kh, broken);
+            if (a.nch > 1) wait_ready(a, b, 1, kh, broken);
             ops_dma(0);
             ops_dma(1);
+            // the stamp of chunk cc + 2 is requested an iteration before it is needed
+            unsigned int stamp_next = a.stamp;
+            auto stamp_request = [&](int cc) __attribute__((always_inline)) {
+                stamp_next = cc < a.nch ? __hip_atomic_load(ready_word(a, b, cc, kh), __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : a.stamp;
+            };
+            stamp_request(2);
             rows_dma(a.v, 0, sRawV);
             rows_dma(a.v, 1, sRawV + kC * BV);
             rows_dma(a.v, 2, sRawV + 2 * kC * BV);
@@ -864,6 +931,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __builtin_amdgcn_s_barrier();
             for (int c = 0; c <= last; ++c) {
                 // this iteration's group: operands of chunk c+2, raw v of chunk c+3, z of chunk c-1-kLag
+                if (c + 2 < a.nch && !stamp_ok(a, stamp_next)) wait_ready(a, b, c + 2, kh, broken);
+                stamp_request(c + 3);
                 ops_dma(c + 2);
                 rows_dma(a.v, c + 3, sRawV + mod3(c + 3) * kC * BV);
                 rows_dma(zsrc, c - 1 - kLag, sZ + mod3(c - 1 - kLag) * kC * BV);
@@ -1081,9 +1150,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+struct ChainLaunch {
+    const void *fn;
+    size_t lds;
+    int grid, ncu;
+};
+
+// Compute units left to the prep kernel before it may run beside the sequential pass.
+constexpr int kPrepCUs = 16;
+
 template <int NT>
-int launch_chain(const ChainArgs &base, hipStream_t stream) {
-    ChainArgs a = base;
+int chain_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
     constexpr size_t lds = ChainLds<NT>::bytes;
     auto fn = chain_kernel<NT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1103,11 +1180,11 @@ int launch_chain(const ChainArgs &base, hipStream_t stream) {
     // queue from blocking all slots.
     const int cap = ncu * per_cu;
     if (cap < 8 * NSL) return fail("chain_kernel: fewer resident workgroup slots than eight heads' slices");
-    const int grid = a.n_items < cap ? a.n_items : cap;
-    a.grid = grid;
-    void *args[] = {&a};
-    e = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3(grid), dim3(512), args, lds, stream);
-    return e == hipSuccess ? 0 : fail("hipLaunchKernel(chain_kernel)", e);
+    cl->fn = reinterpret_cast<const void *>(fn);
+    cl->lds = lds;
+    cl->grid = a.n_items < cap ? a.n_items : cap;
+    cl->ncu = ncu;
+    return 0;
 }
 
 } // namespace
@@ -1121,53 +1198,127 @@ int plan_prefill(int B, int T, int Hk, int Hv, PrefillPlan *plan) {
     plan->nchunks = (T + kC - 1) / kC;
     plan->qk_bytes = align256((size_t)B * plan->nchunks * Hk * kQKF * sizeof(_Float16));
     plan->tp_bytes = align256((size_t)B * plan->nchunks * Hv * kTPF * sizeof(_Float16));
+    plan->ready_bytes = align256((size_t)B * plan->nchunks * Hk * sizeof(unsigned int));
     plan->mbox_bytes = align256((size_t)chains * kTiles * kRing * kC * sizeof(unsigned long long)) +
                        align256((size_t)chains * sizeof(unsigned int)) + 256;
-    plan->total_bytes = plan->qk_bytes + plan->tp_bytes + plan->mbox_bytes;
+    plan->total_bytes = plan->qk_bytes + plan->tp_bytes + plan->ready_bytes + plan->mbox_bytes;
     return 0;
 }
+
+namespace {
+
+// A second stream per device for the prep kernel, so that it can run beside the
+// sequential pass on the compute units the latter leaves free, and two events
+// that order it with the caller's stream.  Created on first use, kept for the
+// life of the process, default priority.
+// The enqueue sequence that uses them runs under the device's lock, so that
+// calls from several host threads cannot interleave their event records.
+struct SideStream {
+    std::mutex mu;
+    hipStream_t s = nullptr;
+    hipEvent_t in = nullptr, done = nullptr;
+};
+
+// Returns the device's side stream (created on first use); the caller holds ss->mu.
+int side_stream(int dev, SideStream **out) {
+    static SideStream per_dev[64];
+    if (dev < 0 || dev >= 64) return fail("prefill: device index out of range for the side stream");
+    SideStream &ss = per_dev[dev];
+    if (!ss.s) {
+        hipError_t e;
+        if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess)
+            return fail("hipStreamCreateWithFlags(prep stream)", e);
+        if ((e = hipEventCreateWithFlags(&ss.in, hipEventDisableTiming)) != hipSuccess)
+            return fail("hipEventCreateWithFlags", e);
+        if ((e = hipEventCreateWithFlags(&ss.done, hipEventDisableTiming)) != hipSuccess)
+            return fail("hipEventCreateWithFlags", e);
+    }
+    *out = &ss;
+    return 0;
+}
+
+} // namespace
 
 int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream) {
     unsigned char *ws = static_cast<unsigned char *>(p.workspace);
     _Float16 *qkf = reinterpret_cast<_Float16 *>(ws);
     _Float16 *tpf = reinterpret_cast<_Float16 *>(ws + plan.qk_bytes);
-    unsigned char *mb = ws + plan.qk_bytes + plan.tp_bytes;
+    unsigned int *ready = reinterpret_cast<unsigned int *>(ws + plan.qk_bytes + plan.tp_bytes);
+    unsigned char *mb = ws + plan.qk_bytes + plan.tp_bytes + plan.ready_bytes;
     const size_t chains = (size_t)p.B * p.Hv;
     const size_t mbox_sz = align256(chains * kTiles * kRing * kC * sizeof(unsigned long long));
     unsigned int *counters = reinterpret_cast<unsigned int *>(mb + mbox_sz);
     // last 256 bytes: error word, then the eight queue tickets and the exit count
     unsigned int *err = reinterpret_cast<unsigned int *>(mb + mbox_sz + align256(chains * sizeof(unsigned int)));
+    // Every call gets a stamp no earlier call in this process had; a zero-filled
+    // workspace holds none (stamps start at 1 and compare modulo 2^32).
+    static std::atomic<unsigned int> call_count{0};
+    unsigned int stamp = call_count.fetch_add(1u) + 1u;
+    if (stamp == 0u) stamp = call_count.fetch_add(1u) + 1u;
 
     PrepArgs pa;
     pa.q = p.q; pa.k = p.k; pa.conv_w = p.conv_w; pa.conv_state_in = p.conv_state_in;
     pa.g = p.g; pa.beta = p.beta; pa.conv_state_out = p.conv_state_out;
-    pa.qkf = qkf; pa.tpf = tpf;
+    pa.qkf = qkf; pa.tpf = tpf; pa.ready = ready; pa.stamp = stamp;
     pa.B = p.B; pa.T = p.T; pa.Hk = p.Hk; pa.Hv = p.Hv; pa.r = p.Hv / p.Hk;
     pa.Cc = 2 * p.Hk * kD + p.Hv * kD; pa.conv = p.conv_width == 4; pa.nch = plan.nchunks;
     pa.eps_l2 = p.eps_l2;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)PrepLds::bytes(p.Hv / p.Hk));
-    if (e != hipSuccess) return fail("hipFuncSetAttribute(chunk_prep_kernel)", e);
-    void *pargs[] = {&pa};
-    e = hipLaunchKernel(reinterpret_cast<const void *>(chunk_prep_kernel),
-                        dim3((unsigned)plan.nchunks, (unsigned)p.Hk, (unsigned)p.B), dim3(256), pargs, PrepLds::bytes(p.Hv / p.Hk),
-                        stream);
-    if (e != hipSuccess) return fail("hipLaunchKernel(chunk_prep_kernel)", e);
 
     ChainArgs a;
     a.qkf = qkf; a.tpf = tpf;
     a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w; a.conv_state_in = p.conv_state_in;
     a.state_in = p.state_in; a.o = p.o; a.conv_state_out = p.conv_state_out; a.state_out = p.state_out;
     a.mbox = reinterpret_cast<unsigned long long *>(mb); a.counters = counters; a.err = err;
-    a.tickets = err + 16; a.exits = err + 32;
+    a.tickets = err + 16; a.exits = err + 32; a.ready = ready; a.stamp = stamp;
     a.B = p.B; a.T = p.T; a.Hk = p.Hk; a.Hv = p.Hv; a.r = pa.r; a.Cc = pa.Cc; a.conv = pa.conv; a.norm = p.norm;
     a.nch = plan.nchunks; a.n_items = (int)(chains * plan.nslice); a.grid = 0;
     a.eps_norm = p.eps_norm;
-    switch (plan.nt) {
-    case 1: return launch_chain<1>(a, stream);
-    case 2: return launch_chain<2>(a, stream);
-    default: return fail("prefill plan: unsupported value-tile count");
+
+    ChainLaunch cl;
+    int rc = plan.nt == 1 ? chain_launch_shape<1>(a, &cl) : plan.nt == 2 ? chain_launch_shape<2>(a, &cl)
+                                                                         : fail("prefill plan: unsupported value-tile count");
+    if (rc) return rc;
+    a.grid = cl.grid;
+
+    // The prep kernel runs beside the sequential pass when the latter leaves
+    // compute units free (it never waits for the sequential pass, so it always
+    // finishes); otherwise the two run one after the other on the caller's stream.
+    // Prep is enqueued first either way: if both streams share a hardware queue,
+    // the sequential pass simply starts after it.
+    const bool beside = cl.grid + kPrepCUs <= cl.ncu;
+    hipStream_t ps = stream;
+    SideStream *ss = nullptr;
+    std::unique_lock<std::mutex> lock;
+    hipError_t e;
+    if (beside) {
+        int dev = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess) return fail("hipGetDevice", e);
+        static std::mutex create_mu;
+        {
+            std::lock_guard<std::mutex> g(create_mu);
+            if ((rc = side_stream(dev, &ss))) return rc;
+        }
+        lock = std::unique_lock<std::mutex>(ss->mu);
+        if ((e = hipEventRecord(ss->in, stream)) != hipSuccess) return fail("hipEventRecord", e);
+        if ((e = hipStreamWaitEvent(ss->s, ss->in, 0)) != hipSuccess) return fail("hipStreamWaitEvent", e);
+        ps = ss->s;
     }
+    const size_t plds = PrepLds::bytes(pa.r);
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds)) != hipSuccess)
+        return fail("hipFuncSetAttribute(chunk_prep_kernel)", e);
+    void *pargs[] = {&pa};
+    if ((e = hipLaunchKernel(reinterpret_cast<const void *>(chunk_prep_kernel),
+                             dim3((unsigned)(plan.nchunks * p.Hk), (unsigned)p.B), dim3(256), pargs, plds, ps)) !=
+        hipSuccess)
+        return fail("hipLaunchKernel(chunk_prep_kernel)", e);
+    if (beside && (e = hipEventRecord(ss->done, ps)) != hipSuccess) return fail("hipEventRecord", e);
+    void *cargs[] = {&a};
+    if ((e = hipLaunchKernel(cl.fn, dim3(cl.grid), dim3(512), cargs, cl.lds, stream)) != hipSuccess)
+        return fail("hipLaunchKernel(chain_kernel)", e);
+    // the caller's stream completes only after both kernels
+    if (beside && (e = hipStreamWaitEvent(stream, ss->done, 0)) != hipSuccess) return fail("hipStreamWaitEvent", e);
+    return 0;
 }
 
 } // namespace gdn

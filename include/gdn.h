@@ -83,9 +83,12 @@ int gdn_state_init(const gdn_shape *shape, float *state, uint16_t *conv_state, v
  * computes for the sequential pass of another: the normalised q/k rows (fp16,
  * B*T*Hk*2*Dk values), per (chunk, value head) the packed lower-triangular
  * T diag(beta) and (Q K^T) o R blocks and the decay vectors ("How Qwen3.5
- * works" §9.11), and an exchange area: the per-row sums of squares that the
- * workgroups sharing one head trade for the gated RMSNorm, work-queue tickets
- * and an error word.  Returns GDN_EINVAL for a shape gdn_prefill would reject.
+ * works" §9.11), one readiness word per (sequence, chunk, key head) through
+ * which the sequential pass follows the kernel that computes those operands
+ * (the two may run at the same time), and an exchange area: the per-row sums
+ * of squares that the workgroups sharing one head trade for the gated RMSNorm,
+ * work-queue tickets and an error word.  Returns GDN_EINVAL for a shape
+ * gdn_prefill would reject.
  */
 int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
 
@@ -107,8 +110,10 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
  *                 NULL; must not overlap conv_state_in
  *  workspace      device memory of at least gdn_prefill_workspace_size() bytes.
  *                 It must be zero-filled before its first use; every call that
- *                 completes leaves its exchange area zeroed again.  Calls that
- *                 run concurrently must not share a workspace.
+ *                 completes leaves its exchange area zeroed again and its
+ *                 readiness words holding a per-call stamp that no later call
+ *                 in the process reuses (stamps wrap after 2^31 calls).  Calls
+ *                 that run concurrently must not share a workspace.
  *
  * `o` must not overlap any input.  Returns GDN_OK once the work is enqueued.
  */
