@@ -782,6 +782,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NSL = kTiles / NT;
     constexpr int NCG = BV / 8;                 // 8-column groups per slice row
     constexpr int NV = 8 - 2 * NT - 1;          // VALU helper waves
+    // Helper 0 runs the norm's exchange; helpers 1 and 2 gate; conv(v) runs on the rest
+    // (NT = 1: helpers 3, 4) or, with only three helpers (NT = 2), on all of them.
+    constexpr int kGateLanes = 128;                       // helpers 1, 2
+    constexpr int kConvBase = NT == 1 ? 192 : 0;          // first helper lane that converts v
+    constexpr int kConvLanes = NV * 64 - kConvBase;
+    static_assert(NV >= 3 && (NT == 2 || NV == 5), "helper roles");
     constexpr int NRD = kC * BV * 2 / 1024;     // DMA instructions for 64 rows of raw v (or z) of the slice
     constexpr int GROUP = kOpSlot / 1024 + 2 * NRD;  // DMA instructions the load wave issues per iteration
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -960,23 +966,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                           h * kD + sv0 + cg * 8);
                 *reinterpret_cast<uint4 *>(sHalo + r3 * BV + cg * 8) = rw;
             }
-            // A lane always serves the same 8-column group (NV * 64 is a multiple of NCG), so its
-            // conv taps and norm weights live in registers once the prologue has staged them.
+            // A lane always serves the same 8-column group (every helper role's lane count is a
+            // multiple of 64, hence of NCG), so its conv taps and norm weights live in registers
+            // once the prologue has staged them.
             const int cgl = vtid % NCG;
             float hw[32], nw[8];
             // conv + SiLU of v for chunk cc (raw slot cc % 3, the three rows before it from
             // sHalo[cc & 1]) -> sV[cc & 1]; the chunk's last three rows -> sHalo[(cc + 1) & 1]
             auto conv_v = [&](int cc) __attribute__((always_inline)) {
+                if (vtid < kConvBase) return;  // not a converting helper
                 _Float16 *dst = sV + (cc & 1) * BV * P64 + cgl * 8 * P64;
                 const uint16_t *cur = sRawV + mod3(cc) * kC * BV + cgl * 8;
                 const uint16_t *prev = sHalo + (cc & 1) * 3 * BV + cgl * 8 - (kC - 3) * BV;  // row kC+r2 -> halo row 3+r2
-                if (vtid < 3 * NCG) {
-                    const int r3 = vtid / NCG, cg = vtid % NCG;
+                if (vtid - kConvBase >= 0 && vtid - kConvBase < 3 * NCG) {
+                    const int r3 = (vtid - kConvBase) / NCG, cg = vtid % NCG;
                     *reinterpret_cast<uint4 *>(sHalo + ((cc + 1) & 1) * 3 * BV + r3 * BV + cg * 8) =
                         *reinterpret_cast<const uint4 *>(sRawV + mod3(cc) * kC * BV + (kC - 3 + r3) * BV + cg * 8);
                 }
 #pragma unroll 1
-                for (int it = vtid; it < kC * NCG; it += NV * 64) {
+                for (int it = vtid - kConvBase; it < kC * NCG; it += kConvLanes) {
                     const int row = it / NCG;
                     uint4 rw[4];
 #pragma unroll
@@ -1015,7 +1023,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const float *rs = sRstd + (oc & 1) * kC;
                 const uint16_t *zt = sZ + mod3(oc) * kC * BV + cgl * 8;
 #pragma unroll 1
-                for (int it = vtid - 64; it < kC * NCG; it += (NV - 1) * 64) {
+                for (int it = vtid - 64; it < kC * NCG; it += kGateLanes) {
                     const int row = it / NCG;
                     const int tt = oc * kC + row;
                     float y[8];
@@ -1094,14 +1102,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                     mb_request(rc + 1);
-                    if (c + 1 < a.nch) conv_v(c + 1);
+                    if (kConvBase == 0 && c + 1 < a.nch) conv_v(c + 1);
                     lds_barrier();
                 }
             } else {
                 for (int c = 0; c <= last; ++c) {
-                    if (c + 1 < a.nch) conv_v(c + 1);
+                    if (vtid >= kConvBase && c + 1 < a.nch) conv_v(c + 1);
                     const int oc = c - 3 - kLag;
-                    if (oc >= 0 && oc < a.nch) gate(oc);
+                    if (vtid < 64 + kGateLanes && oc >= 0 && oc < a.nch) gate(oc);
                     lds_barrier();
                 }
             }
