@@ -783,9 +783,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NCG = BV / 8;                 // 8-column groups per slice row
     constexpr int NV = 8 - 2 * NT - 1;          // VALU helper waves
     // Helper 0 runs the norm's exchange; helpers 1 and 2 gate; conv(v) runs on the rest
-    // (NT = 1: helpers 3, 4) or, with only three helpers (NT = 2), on all of them.
+    // (NT = 1: helpers 3, 4) or, with only three helpers (NT = 2), on helpers 1 and 2.
     constexpr int kGateLanes = 128;                       // helpers 1, 2
-    constexpr int kConvBase = NT == 1 ? 192 : 0;          // first helper lane that converts v
+    constexpr int kConvBase = NT == 1 ? 192 : 64;         // first helper lane that converts v
     constexpr int kConvLanes = NV * 64 - kConvBase;
     static_assert(NV >= 3 && (NT == 2 || NV == 5), "helper roles");
     constexpr int NRD = kC * BV * 2 / 1024;     // DMA instructions for 64 rows of raw v (or z) of the slice
@@ -803,8 +803,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches are scalar
     const int l16 = lane & 15, lq = lane >> 4;
-    const bool is_a = wave < NT, is_b = wave >= NT && wave < 2 * NT, is_l = wave == 2 * NT;
-    const int vh = wave - 2 * NT - 1;  // VALU-helper index (valid when >= 0)
+    // Waves w and w + 4 share a SIMD.  The state waves (0 .. NT-1) are paired with the lightest
+    // roles: the load wave and helper 0 (the norm exchange) sit at 2 NT and 2 NT + 1.
+    const bool is_a = wave < NT, is_b = wave >= NT && wave < 2 * NT, is_l = wave == 2 * NT + 1;
+    const int vh = wave == 2 * NT ? 0 : wave - 2 * NT - 1;  // VALU-helper index (valid when >= 0)
     int broken = 0;
     __shared__ int s_item;
     // Work items (chain, slice) come from eight queues, one per XCD: chain c
@@ -1102,7 +1104,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                     mb_request(rc + 1);
-                    if (kConvBase == 0 && c + 1 < a.nch) conv_v(c + 1);
                     lds_barrier();
                 }
             } else {
