@@ -52,6 +52,7 @@
 // All contractions use fp16 MFMA operands with fp32 accumulation; the state is
 // carried in fp32 across chunks; inputs and outputs are bf16.
 #include <atomic>
+#include <cstdlib>
 #include <mutex>
 
 #include "gdn_device.h"
@@ -1246,6 +1247,16 @@ int side_stream(int dev, SideStream **out) {
     return 0;
 }
 
+// Running the two kernels side by side needs the device to run them at the same
+// time.  A counter-collecting profiler (rocprofv3 --pmc, which sets
+// ROCPROF_COUNTERS) serialises every dispatch and may start the sequential pass
+// first, which would then wait out its bounded waits for stamps that cannot come;
+// such runs, and any run with GDN_PREFILL_SEQUENTIAL set, use one stream.
+bool beside_allowed() {
+    static const bool ok = !std::getenv("ROCPROF_COUNTERS") && !std::getenv("GDN_PREFILL_SEQUENTIAL");
+    return ok;
+}
+
 } // namespace
 
 int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream) {
@@ -1294,7 +1305,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     // finishes); otherwise the two run one after the other on the caller's stream.
     // Prep is enqueued first either way: if both streams share a hardware queue,
     // the sequential pass simply starts after it.
-    const bool beside = cl.grid + kPrepCUs <= cl.ncu;
+    const bool beside = cl.grid + kPrepCUs <= cl.ncu && beside_allowed();
     hipStream_t ps = stream;
     SideStream *ss = nullptr;
     std::unique_lock<std::mutex> lock;

@@ -7,6 +7,8 @@
   fresh workspace, bit for bit (the exchange area is left clean).
 - Repeated calls are deterministic; state_out may alias state_in.
 - gdn_state_init zeroes the state and the conv state.
+- One stream (prep, then the sequential pass) gives the same bits as the prep
+  kernel running beside the sequential pass.
 """
 import numpy as np
 import pytest
@@ -148,3 +150,41 @@ def test_state_init_zeroes():
     gdn.gdn_state_init(shape, st, None)
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(st)) == 0
+
+
+_SEQ_CHILD = r"""
+import sys, numpy as np
+sys.path.insert(0, sys.argv[1])
+import gdn_inputs as GI
+import gdn_run as R
+import torch
+w = GI.Workload("seq_mode", 2, 200, 2, 4, random_state=True, random_conv_state=True, tag=703)
+r = R.Prefill(GI.make_inputs(w), 2, 200, 2, 4, True, True)
+r.run()
+torch.cuda.synchronize()
+assert r.exchange_error_word() == 0
+np.savez(sys.argv[2], o=R.bits(r.o), s=r.state_out.cpu().numpy(), cs=R.bits(r.conv_state_out))
+"""
+
+
+def test_sequential_mode_matches_side_by_side(tmp_path):
+    """GDN_PREFILL_SEQUENTIAL=1 (one stream, prep then chain) gives the same bits as
+    the default, where the prep kernel may run beside the sequential pass."""
+    R = _R()
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = str(tmp_path / "seq.npz")
+    env = dict(os.environ, GDN_PREFILL_SEQUENTIAL="1")
+    print("[seam] sequential-mode child process", flush=True)
+    subprocess.run([sys.executable, "-c", _SEQ_CHILD, root, out], env=env, check=True, timeout=300)
+    w = GI.Workload("seq_mode", 2, 200, 2, 4, random_state=True, random_conv_state=True, tag=703)
+    r = R.Prefill(GI.make_inputs(w), 2, 200, 2, 4, True, True)
+    r.run()
+    torch.cuda.synchronize()
+    assert r.exchange_error_word() == 0
+    ref = np.load(out)
+    np.testing.assert_array_equal(R.bits(r.o), ref["o"])
+    np.testing.assert_array_equal(r.state_out.cpu().numpy(), ref["s"])
+    np.testing.assert_array_equal(R.bits(r.conv_state_out), ref["cs"])
