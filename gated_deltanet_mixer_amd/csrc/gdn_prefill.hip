@@ -577,6 +577,13 @@ struct ChainLds {
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
+// Position in LDS of the 16-byte piece of k^ fragment lane L = 16 b + 4 c + a:
+// 16 b + 4 (c ^ b) + a (an involution).  The transposing reads of the state update
+// take, per 16-lane group, the pieces of lanes 4 c + a + 16 b for one c; stored in
+// lane order those pieces fall on only four bank groups, swizzled on sixteen, and
+// the plain 16-lane phases of the operand reads stay conflict-free as well.
+__device__ __forceinline__ int kswz(int L) { return (L & 0x33) | ((((L >> 2) ^ (L >> 4)) & 3) << 2); }
+
 // Operands of one chunk that the state wave keeps in registers (loaded one
 // chunk ahead): T diag(beta) fragments and the decay vectors.
 struct StateFrags {
@@ -614,7 +621,7 @@ __device__ __forceinline__ void state_step(unsigned char *smem, floatx4 (&S)[8],
 
     half8 fk[16];
 #pragma unroll
-    for (int f = 0; f < 16; ++f) fk[f] = *reinterpret_cast<const half8 *>(op + f * 1024 + lane * 16);
+    for (int f = 0; f < 16; ++f) fk[f] = *reinterpret_cast<const half8 *>(op + f * 1024 + kswz(lane) * 16);
     half4 vv[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) vv[I] = lds_half4(sVc + jc * P64 + 16 * I + 4 * lq);
@@ -750,6 +757,7 @@ __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, u
 
 __device__ __forceinline__ int mod3(int x) { return ((x % 3) + 3) % 3; }
 
+
 // The prep kernel may still be running while this one starts: prep block
 // (sequence b, chunk cc, key head kh) stores this call's stamp once its operands
 // are written back (agent-scope release).  A chunk's operands are first touched
@@ -853,8 +861,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // ---------------------------------------------------------- state wave
             const int jc = 16 * wave + l16;
             // transposing-read lane offset (fp16 elements): row j = l16 / 4 of the 16-lane
-            // group, 4-key chunk q = l16 % 4 -> k^ fragment lane (4 lq + j) + 16 q
-            const int trofs = ((4 * lq + (l16 >> 2)) + 16 * (l16 & 3)) * 8;
+            // group, 4-key chunk q = l16 % 4 -> k^ fragment lane (4 lq + j) + 16 q, at its
+            // swizzled LDS position
+            const int trofs = kswz((4 * lq + (l16 >> 2)) + 16 * (l16 & 3)) * 8;
             StateFrags fr;
             wait_ready(a, b, 0, kh, broken);
             state_load(fr, tp0, lane, lq);
@@ -914,7 +923,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 unsigned char *slot = smem + L::sOp + (cc % kDma) * kOpSlot;
                 const _Float16 *kb = qk0 + cl * qk_stride + kKOff;
 #pragma unroll
-                for (int f = 0; f < 16; ++f) dma16(kb + f * kFrag + lane * 8, slot + f * 1024);
+                for (int f = 0; f < 16; ++f) dma16(kb + f * kFrag + kswz(lane) * 8, slot + f * 1024);
             };
             const uint16_t *zsrc = a.norm ? a.z : a.v;
             // prologue: operands of chunks 0 and 1, raw v of chunks 0..2.  The load wave is
