@@ -933,31 +933,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (a.nch > 1) wait_ready(a, b, 1, kh, broken);
             ops_dma(0);
             ops_dma(1);
-            // the stamp of chunk cc + 2 is requested an iteration before it is needed
-            unsigned int stamp_next = a.stamp;
-            auto stamp_request = [&](int cc) __attribute__((always_inline)) {
-                stamp_next = cc < a.nch ? __hip_atomic_load(ready_word(a, b, cc, kh), __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT)
-                                        : a.stamp;
+            // a chunk's stamp is requested two iterations before it is needed, so that waiting
+            // for the previous iteration's DMA group never waits for a stamp load as well
+            auto stamp_load = [&](int cc) __attribute__((always_inline)) {
+                return cc < a.nch ? __hip_atomic_load(ready_word(a, b, cc, kh), __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : a.stamp;
             };
-            stamp_request(2);
+            // two stamp registers used in turn (iteration c reads and refills the one of its
+            // parity), so no in-flight load is ever copied between registers
+            unsigned int stamp_e = stamp_load(2), stamp_o = stamp_load(3);  // chunk c+2 for even / odd c
             rows_dma(a.v, 0, sRawV);
             rows_dma(a.v, 1, sRawV + kC * BV);
             rows_dma(a.v, 2, sRawV + 2 * kC * BV);
             wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_s_barrier();
-            for (int c = 0; c <= last; ++c) {
+            auto iter = [&](int c, unsigned int &st) __attribute__((always_inline)) {
+                // (kept in program order: a stamp test moved into the previous iteration's DMA
+                // group would make the wave wait for that whole group)
+                __builtin_amdgcn_sched_barrier(0);
                 // this iteration's group: operands of chunk c+2, raw v of chunk c+3, z of chunk c-1-kLag
-                if (c + 2 < a.nch && !stamp_ok(a, stamp_next)) wait_ready(a, b, c + 2, kh, broken);
-                stamp_request(c + 3);
+                if (c + 2 < a.nch && !stamp_ok(a, st)) wait_ready(a, b, c + 2, kh, broken);
+                st = stamp_load(c + 4);
                 ops_dma(c + 2);
                 rows_dma(a.v, c + 3, sRawV + mod3(c + 3) * kC * BV);
                 rows_dma(zsrc, c - 1 - kLag, sZ + mod3(c - 1 - kLag) * kC * BV);
-                // the previous iteration's group (chunk c+1) has landed
-                wait_vmcnt<GROUP>();
+                // the previous iteration's group (chunk c+1) has landed (this iteration's stamp
+                // load and group may still be in flight)
+                wait_vmcnt<GROUP + 1>();
                 __builtin_amdgcn_s_barrier();
+            };
+            int c = 0;
+            for (; c + 1 <= last; c += 2) {
+                iter(c, stamp_e);
+                iter(c + 1, stamp_o);
             }
+            if (c <= last) iter(c, stamp_e);
             wait_vmcnt<0>();
         } else {
             // ---------------------------------------------------------- VALU helpers
