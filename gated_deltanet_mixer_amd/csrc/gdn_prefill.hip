@@ -813,9 +813,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches are scalar
     const int l16 = lane & 15, lq = lane >> 4;
     // Waves w and w + 4 share a SIMD.  The state waves (0 .. NT-1) are paired with the lightest
-    // roles: the load wave and helper 0 (the norm exchange) sit at 2 NT and 2 NT + 1.
-    const bool is_a = wave < NT, is_b = wave >= NT && wave < 2 * NT, is_l = wave == 2 * NT + 1;
-    const int vh = wave == 2 * NT ? 0 : wave - 2 * NT - 1;  // VALU-helper index (valid when >= 0)
+    // roles, the load wave and helper 0 (the norm exchange): with NT = 2 they sit at 4 and 5,
+    // with NT = 1 the load wave sits at 4 (beside the state wave) and helper 0 at 5 (beside the
+    // read-out wave); the other helpers take the remaining waves in order.
+    constexpr int kLoadWave = NT == 1 ? 4 : 5, kNormWave = NT == 1 ? 5 : 4;
+    const bool is_a = wave < NT, is_b = wave >= NT && wave < 2 * NT, is_l = wave == kLoadWave;
+    const int vh = wave == kNormWave ? 0
+                   : NT == 1     ? (wave < 4 ? wave - 1 : wave - 3)   // 2, 3, 6, 7 -> 1, 2, 3, 4
+                                 : wave - 5;                          // 6, 7 -> 1, 2
     int broken = 0;
     __shared__ int s_item;
     // Work items (chain, slice) come from eight queues, one per XCD: chain c
