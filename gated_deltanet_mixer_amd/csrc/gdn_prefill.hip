@@ -1155,12 +1155,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
 
-        // ---- the last slice of a chain to finish clears the chain's mailbox
+        // ---- the last slice of a chain to finish clears the chain's mailbox.  Relaxed order
+        // suffices and avoids an L2 write-back per item: every mailbox word is accessed only by
+        // agent-scope atomics, and a slice's last mailbox read has returned (its value was used
+        // before the loop's final barrier) before its count goes up.
         if (a.norm) {
             __shared__ unsigned int last_one;
             if (tid == 0) {
                 const unsigned int old =
-                    __hip_atomic_fetch_add(a.counters + chain, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(a.counters + chain, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 last_one = (old == NSL - 1) ? 1u : 0u;
             }
             lds_barrier();
@@ -1173,10 +1176,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         lds_barrier();
     }
-    // the last workgroup out rewinds the queues for the next launch
+    // the last workgroup out rewinds the queues for the next launch (its own ticket requests
+    // have returned before its exit is counted, so relaxed order suffices here too)
     if (tid == 0) {
         const unsigned int done =
-            __hip_atomic_fetch_add(a.exits, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(a.exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (done == (unsigned int)a.grid - 1) {
             for (int q = 0; q < 8; ++q) __hip_atomic_store(a.tickets + q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(a.exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
