@@ -837,16 +837,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     for (;;) {
         if (tid == 0) {
+            auto queue_len = [&](int q) { return (unsigned int)((n_chains > q ? (n_chains - q + 7) / 8 : 0) * NSL); };
             int item = -1;
-            for (; qi < 8 && item < 0; ) {
+            while (qi < 8 && item < 0) {
                 const int q = (xcc + qi) & 7;
-                const int nq = n_chains > q ? (n_chains - q + 7) / 8 : 0;
                 const unsigned int tk = __hip_atomic_fetch_add(a.tickets + q, 1u, __ATOMIC_RELAXED,
                                                                __HIP_MEMORY_SCOPE_AGENT);
-                if (tk < (unsigned int)(nq * NSL))
+                if (tk < queue_len(q)) {
                     item = (q + 8 * (int)(tk / NSL)) * NSL + (int)(tk % NSL);
-                else
+                } else {
+                    // queue q is used up (tickets only grow during a launch): read every queue's
+                    // count at once, one memory latency, and skip to the first that still has
+                    // items, if any, instead of trying the queues one atomic at a time
+                    unsigned int seen[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        seen[j] = __hip_atomic_load(a.tickets + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     ++qi;
+                    while (qi < 8 && seen[(xcc + qi) & 7] >= queue_len((xcc + qi) & 7)) ++qi;
+                }
             }
             s_item = item;
         }
@@ -1175,6 +1184,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
         lds_barrier();
+        // with no more items than workgroups, every item has a workgroup of its own (each one
+        // that has not started yet takes one when it does), so a finished workgroup leaves
+        if (a.n_items <= a.grid) break;
     }
     // the last workgroup out rewinds the queues for the next launch (its own ticket requests
     // have returned before its exit is counted, so relaxed order suffices here too)
