@@ -101,6 +101,22 @@ def run_prefill(gdn, d):
                     None, None, d["o"], d["state_out"], d["conv_state_out"], d["ws"])
 
 
+def add_gate_logits(torch, d, Hv, seed):
+    """Gate logits in place of g and beta: a, b ~ N(0, 1), A_log = ln U(1, 16), dt_bias ~ U(-6.9, -2.3)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    d["a"] = torch.randn(d["g"].shape, generator=gen, device="cuda")
+    d["b"] = torch.randn(d["beta"].shape, generator=gen, device="cuda")
+    d["A_log"] = torch.log(torch.rand((Hv,), generator=gen, device="cuda") * 15.0 + 1.0)
+    d["dt_bias"] = torch.rand((Hv,), generator=gen, device="cuda") * 4.6 - 6.9
+
+
+def run_prefill_gate_logits(gdn, d):
+    gdn.gdn_prefill_gate_logits(d["shape"], d["q"], d["k"], d["v"], d["a"], d["b"], d["A_log"], d["dt_bias"],
+                                d["z"], d["conv_w"], d["norm_w"], None, None, d["o"], d["state_out"],
+                                d["conv_state_out"], d["ws"])
+
+
 def time_calls(torch, fn, sets, steps, warmup):
     """Average ms per call over `steps` calls (cycling the input sets), with
     HIP events on the current stream, bracketed by device syncs."""
@@ -118,17 +134,22 @@ def time_calls(torch, fn, sets, steps, warmup):
     return start.elapsed_time(end) / steps, t_wall
 
 
-def bench_prefill(torch, gdn, name, steps, warmup):
+def bench_prefill(torch, gdn, name, steps, warmup, gate_logits=False):
     B, T, Hk, Hv = WORKLOADS[name]
     per_set = prefill_bytes(B, T, Hk, Hv) + B * T * Hk * 2 * D * 2
     nsets = max(1, min(4, math.ceil(320e6 / per_set)))  # rotate past the 256 MB Infinity Cache
     sets = [make_prefill_set(torch, gdn, B, T, Hk, Hv, seed=1000 + i) for i in range(nsets)]
+    if gate_logits:
+        for i, d in enumerate(sets):
+            add_gate_logits(torch, d, Hv, seed=2000 + i)
     torch.cuda.synchronize()
-    ms, wall = time_calls(torch, lambda d: run_prefill(gdn, d), sets, steps, warmup)
+    run = run_prefill_gate_logits if gate_logits else run_prefill
+    ms, wall = time_calls(torch, lambda d: run(gdn, d), sets, steps, warmup)
     nbytes = prefill_bytes(B, T, Hk, Hv)
     flops = USEFUL_FLOP_PER_TOKEN_HEAD * B * T * Hv
     res = {
-        "workload": name, "B": B, "T": T, "Hk": Hk, "Hv": Hv, "ms_per_call": ms,
+        "workload": name + (" (gdn_prefill_gate_logits)" if gate_logits else ""), "B": B, "T": T, "Hk": Hk,
+        "Hv": Hv, "ms_per_call": ms,
         "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
         "hbm_GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / HBM_PEAK,
         "useful_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_useful_frac": flops / (ms * 1e-3) / MFMA_FP16_PEAK,
@@ -275,6 +296,9 @@ def main(argv=None):
                 B, T, Hk, Hv = WORKLOADS[name]
                 steps = max(3, min(args.steps, int(2e8 // (B * T * Hv))))
                 extra[name] = bench_prefill(torch, gdn, name, steps, 2)
+        # the same layer through the entry point that takes the gate logits
+        extra[args.workload + "_gate_logits"] = bench_prefill(torch, gdn, args.workload, max(20, args.steps // 4), 5,
+                                                              gate_logits=True)
     B, T, Hk, Hv = WORKLOADS[args.workload]
     out = {
         "metric": "GDN prefill tokens/s per layer (% MFMA peak); decode-step state GB/s (% HBM)",

@@ -64,9 +64,11 @@ _lib.gdn_state_init.argtypes = [_sp, _vp, _vp, _vp]
 _lib.gdn_prefill_workspace_size.argtypes = [_sp, C.POINTER(C.c_size_t)]
 _lib.gdn_prefill.argtypes = [_sp] + [_vp] * 14 + [C.c_size_t, _vp]
 _lib.gdn_decode_step.argtypes = [_sp] + [_vp] * 12
+_lib.gdn_prefill_gate_logits.argtypes = [_sp] + [_vp] * 16 + [C.c_size_t, _vp]
+_lib.gdn_decode_step_gate_logits.argtypes = [_sp] + [_vp] * 14
 
 EXPORTED = ("gdn_state_init", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
-            "gdn_status_string", "gdn_last_error")
+            "gdn_prefill_gate_logits", "gdn_decode_step_gate_logits", "gdn_status_string", "gdn_last_error")
 
 
 def _ptr(t):
@@ -125,3 +127,23 @@ def gdn_decode_step(shape: gdn_shape, q, k, v, g, beta, z, conv_w, norm_w, state
                               _ptr(conv_w), _ptr(norm_w), _ptr(state), _ptr(conv_state), _ptr(o),
                               _stream(stream))
     _check("gdn_decode_step", rc)
+
+
+def gdn_prefill_gate_logits(shape: gdn_shape, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state_in,
+                            conv_state_in, o, state_out, conv_state_out, workspace,
+                            workspace_bytes: int | None = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.gdn_prefill_gate_logits(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+                                      _ptr(dt_bias), _ptr(z), _ptr(conv_w), _ptr(norm_w), _ptr(state_in),
+                                      _ptr(conv_state_in), _ptr(o), _ptr(state_out), _ptr(conv_state_out),
+                                      _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("gdn_prefill_gate_logits", rc)
+
+
+def gdn_decode_step_gate_logits(shape: gdn_shape, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state,
+                                conv_state, o, stream=None) -> None:
+    rc = _lib.gdn_decode_step_gate_logits(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                          _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(conv_w), _ptr(norm_w),
+                                          _ptr(state), _ptr(conv_state), _ptr(o), _stream(stream))
+    _check("gdn_decode_step_gate_logits", rc)

@@ -83,12 +83,20 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes) {
     return GDN_OK;
 }
 
-int gdn_prefill(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
-                const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
-                const float *state_in, const uint16_t *conv_state_in, uint16_t *o, float *state_out,
-                uint16_t *conv_state_out, void *workspace, size_t workspace_bytes, void *stream) {
+} // extern "C"
+
+namespace {
+
+// g, beta are the gate logits a, b when A_log and dt_bias are given (both or neither).
+int prefill_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                 const float *beta, const float *A_log, const float *dt_bias, const uint16_t *z,
+                 const uint16_t *conv_w, const uint16_t *norm_w, const float *state_in,
+                 const uint16_t *conv_state_in, uint16_t *o, float *state_out, uint16_t *conv_state_out,
+                 void *workspace, size_t workspace_bytes, void *stream) {
     int rc = check_shape(s, true);
     if (rc) return rc;
+    if ((A_log == nullptr) != (dt_bias == nullptr)) return GDN_EINVAL;
+    if (A_log && (!aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_EINVAL;
     const bool norm = !(s->flags & GDN_NO_NORM);
     const bool conv = s->conv_width == 4;
     if (!q || !k || !v || !g || !beta || !o || !state_out || !workspace) return GDN_EINVAL;
@@ -108,7 +116,8 @@ int gdn_prefill(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const 
         const void *p;
         size_t n;
     } inputs[] = {{q, nqk}, {k, nqk}, {v, nv}, {g, ngb}, {beta, ngb}, {norm ? z : nullptr, nv},
-                  {conv_w, nw}, {norm_w, nn}, {state_in, nst}, {conv_state_in, ncs}};
+                  {conv_w, nw}, {norm_w, nn}, {state_in, nst}, {conv_state_in, ncs},
+                  {A_log, Hv * 4}, {dt_bias, Hv * 4}};
     for (const auto &in : inputs)
         if (overlap(o, nv, in.p, in.n) || overlap(workspace, workspace_bytes, in.p, in.n)) return GDN_EINVAL;
     if (overlap(conv_state_out, ncs, conv_state_in, ncs)) return GDN_EINVAL;
@@ -127,18 +136,22 @@ int gdn_prefill(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const 
 
     PrefillParams p;
     p.q = q; p.k = k; p.v = v; p.z = norm ? z : nullptr; p.conv_w = conv_w; p.norm_w = norm ? norm_w : nullptr;
-    p.conv_state_in = conv_state_in; p.g = g; p.beta = beta; p.state_in = state_in;
+    p.conv_state_in = conv_state_in; p.g = g; p.beta = beta; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.state_in = state_in;
     p.o = o; p.conv_state_out = conv_state_out; p.state_out = state_out; p.workspace = workspace;
     p.B = s->B; p.T = s->T; p.Hk = s->Hk; p.Hv = s->Hv; p.conv_width = s->conv_width; p.norm = norm;
     p.eps_l2 = s->eps_l2; p.eps_norm = s->eps_norm;
     return launch_prefill(p, plan, static_cast<hipStream_t>(stream)) ? GDN_EHIP : GDN_OK;
 }
 
-int gdn_decode_step(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
-                    const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
-                    float *state, uint16_t *conv_state, uint16_t *o, void *stream) {
+int decode_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                const float *beta, const float *A_log, const float *dt_bias, const uint16_t *z,
+                const uint16_t *conv_w, const uint16_t *norm_w, float *state, uint16_t *conv_state, uint16_t *o,
+                void *stream) {
     int rc = check_shape(s, false);
     if (rc) return rc;
+    if ((A_log == nullptr) != (dt_bias == nullptr)) return GDN_EINVAL;
+    if (A_log && (!aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_EINVAL;
     const bool norm = !(s->flags & GDN_NO_NORM);
     const bool conv = s->conv_width == 4;
     if (!q || !k || !v || !g || !beta || !o || !state) return GDN_EINVAL;
@@ -158,7 +171,7 @@ int gdn_decode_step(const gdn_shape *s, const uint16_t *q, const uint16_t *k, co
         const void *p;
         size_t n;
     } ro[] = {{q, nqk}, {k, nqk}, {v, nv}, {g, ngb}, {beta, ngb}, {norm ? z : nullptr, nv},
-              {conv_w, nw}, {norm_w, nn}};
+              {conv_w, nw}, {norm_w, nn}, {A_log, Hv * 4}, {dt_bias, Hv * 4}};
     for (const auto &in : ro)
         if (overlap(o, nv, in.p, in.n) || overlap(state, nst, in.p, in.n) || overlap(conv_state, ncs, in.p, in.n))
             return GDN_EINVAL;
@@ -167,10 +180,47 @@ int gdn_decode_step(const gdn_shape *s, const uint16_t *q, const uint16_t *k, co
 
     DecodeParams p;
     p.q = q; p.k = k; p.v = v; p.z = norm ? z : nullptr; p.conv_w = conv_w; p.norm_w = norm ? norm_w : nullptr;
-    p.g = g; p.beta = beta; p.state = state; p.conv_state = conv_state; p.o = o;
+    p.g = g; p.beta = beta; p.A_log = A_log; p.dt_bias = dt_bias;
+    p.state = state; p.conv_state = conv_state; p.o = o;
     p.B = s->B; p.Hk = s->Hk; p.Hv = s->Hv; p.conv_width = s->conv_width; p.norm = norm;
     p.eps_l2 = s->eps_l2; p.eps_norm = s->eps_norm;
     return launch_decode(p, static_cast<hipStream_t>(stream)) ? GDN_EHIP : GDN_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int gdn_prefill(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
+                const float *state_in, const uint16_t *conv_state_in, uint16_t *o, float *state_out,
+                uint16_t *conv_state_out, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(s, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state_in, conv_state_in, o,
+                        state_out, conv_state_out, workspace, workspace_bytes, stream);
+}
+
+int gdn_prefill_gate_logits(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const float *a, const float *b, const float *A_log, const float *dt_bias,
+                            const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
+                            const float *state_in, const uint16_t *conv_state_in, uint16_t *o, float *state_out,
+                            uint16_t *conv_state_out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!A_log || !dt_bias) return GDN_EINVAL;
+    return prefill_impl(s, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state_in, conv_state_in, o, state_out,
+                        conv_state_out, workspace, workspace_bytes, stream);
+}
+
+int gdn_decode_step(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                    const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
+                    float *state, uint16_t *conv_state, uint16_t *o, void *stream) {
+    return decode_impl(s, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state, conv_state, o, stream);
+}
+
+int gdn_decode_step_gate_logits(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                const float *a, const float *b, const float *A_log, const float *dt_bias,
+                                const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w, float *state,
+                                uint16_t *conv_state, uint16_t *o, void *stream) {
+    if (!A_log || !dt_bias) return GDN_EINVAL;
+    return decode_impl(s, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state, conv_state, o, stream);
 }
 
 } // extern "C"

@@ -28,7 +28,8 @@ constexpr int kD = 128;
 
 struct DecodeArgs {
     const uint16_t *q, *k, *v, *z, *conv_w, *norm_w;
-    const float *g, *beta;
+    const float *g, *beta;       // or the gate logits a, b when A_log is set
+    const float *A_log, *dt_bias;
     float *state;
     uint16_t *conv_state, *o;
     int B, Hk, Hv, r, Cc, conv, norm;
@@ -142,8 +143,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         float4 S[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) S[m] = Sp[(rg + 8 * m) * (kD / 4) + jg];
-        const float alpha = __expf(a.g[hb]);
-        const float beta = a.beta[hb];
+        float gl = a.g[hb], beta = a.beta[hb];
+        if (a.A_log) {  // gates from their logits
+            gl = gate_g(gl, a.A_log[h], a.dt_bias[h]);
+            beta = gate_beta(beta);
+        }
+        const float alpha = __expf(gl);
 
         float pk[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 int launch_decode(const DecodeParams &p, hipStream_t stream) {
     DecodeArgs a;
     a.q = p.q; a.k = p.k; a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w;
-    a.g = p.g; a.beta = p.beta; a.state = p.state; a.conv_state = p.conv_state; a.o = p.o;
+    a.g = p.g; a.beta = p.beta; a.A_log = p.A_log; a.dt_bias = p.dt_bias; a.state = p.state; a.conv_state = p.conv_state; a.o = p.o;
     a.B = p.B; a.Hk = p.Hk; a.Hv = p.Hv; a.r = p.Hv / p.Hk;
     a.Cc = 2 * p.Hk * kD + p.Hv * kD;
     a.conv = p.conv_width == 4; a.norm = p.norm;

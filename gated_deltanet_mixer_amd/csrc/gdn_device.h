@@ -61,6 +61,15 @@ __device__ __forceinline__ float silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + t);
 }
 
+// Gates from their logits ("How Qwen3.5 works" §9.5), in fp32:
+// g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b).
+__device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias) {
+    const float x = a + dt_bias;
+    const float sp = x > 20.0f ? x : log1pf(expf(x));  // softplus; ln(1 + e^x) = x to fp32 beyond 20
+    return -expf(A_log) * sp;
+}
+__device__ __forceinline__ float gate_beta(float b) { return 1.0f / (1.0f + expf(-b)); }
+
 // ---------------------------------------------------------------- reductions
 
 // Sum over the 64 lanes of a wave; every lane receives the total.

@@ -6,9 +6,10 @@
 
 namespace gdn {
 
+// g and beta hold the gate logits a and b when A_log and dt_bias are set.
 struct DecodeParams {
     const uint16_t *q, *k, *v, *z, *conv_w, *norm_w;
-    const float *g, *beta;
+    const float *g, *beta, *A_log, *dt_bias;
     float *state;
     uint16_t *conv_state, *o;
     int B, Hk, Hv, conv_width, norm;
@@ -17,7 +18,7 @@ struct DecodeParams {
 
 struct PrefillParams {
     const uint16_t *q, *k, *v, *z, *conv_w, *norm_w, *conv_state_in;
-    const float *g, *beta, *state_in;
+    const float *g, *beta, *A_log, *dt_bias, *state_in;
     uint16_t *o, *conv_state_out;
     float *state_out;
     void *workspace;

@@ -168,7 +168,8 @@ __device__ __forceinline__ half4 lds_tr16(const _Float16 *p) {
 
 struct PrepArgs {
     const uint16_t *q, *k, *conv_w, *conv_state_in;
-    const float *g, *beta;
+    const float *g, *beta;      // or the gate logits a, b when A_log is set
+    const float *A_log, *dt_bias;
     uint16_t *conv_state_out;
     _Float16 *qkf;  // [B][nch][Hk][kQKF]
     _Float16 *tpf;  // [B][nch][Hv][kTPF]
@@ -228,6 +229,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const size_t gi = ((size_t)b * a.T + t) * a.Hv + kh * a.r + i % a.r;
             g_ld[u] = a.g[gi];
             b_ld[u] = a.beta[gi];
+        }
+    }
+    if (a.A_log) {  // gates from their logits
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + 256 * u, h = kh * a.r + i % a.r;
+            if (i < ngb && tc0 + i / a.r < a.T) {
+                g_ld[u] = gate_g(g_ld[u], a.A_log[h], a.dt_bias[h]);
+                b_ld[u] = gate_beta(b_ld[u]);
+            }
         }
     }
 
@@ -338,8 +349,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     for (int i = tid + 512; i < ngb; i += 256) {  // more than 8 value heads per key head
         const int row = i / a.r, t = tc0 + row;
         const size_t gi = ((size_t)b * a.T + t) * a.Hv + kh * a.r + i % a.r;
-        sGr[(i % a.r) * kC + row] = t < a.T ? a.g[gi] : 0.0f;
-        sGr[(a.r + i % a.r) * kC + row] = t < a.T ? a.beta[gi] : 0.0f;
+        const int h = kh * a.r + i % a.r;
+        float gv = t < a.T ? a.g[gi] : 0.0f, bv = t < a.T ? a.beta[gi] : 0.0f;
+        if (a.A_log && t < a.T) {
+            gv = gate_g(gv, a.A_log[h], a.dt_bias[h]);
+            bv = gate_beta(bv);
+        }
+        sGr[(i % a.r) * kC + row] = gv;
+        sGr[(a.r + i % a.r) * kC + row] = bv;
     }
     lds_barrier();
 
@@ -1320,7 +1337,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
 
     PrepArgs pa;
     pa.q = p.q; pa.k = p.k; pa.conv_w = p.conv_w; pa.conv_state_in = p.conv_state_in;
-    pa.g = p.g; pa.beta = p.beta; pa.conv_state_out = p.conv_state_out;
+    pa.g = p.g; pa.beta = p.beta; pa.A_log = p.A_log; pa.dt_bias = p.dt_bias; pa.conv_state_out = p.conv_state_out;
     pa.qkf = qkf; pa.tpf = tpf; pa.ready = ready; pa.stamp = stamp;
     pa.B = p.B; pa.T = p.T; pa.Hk = p.Hk; pa.Hv = p.Hv; pa.r = p.Hv / p.Hk;
     pa.Cc = 2 * p.Hk * kD + p.Hv * kD; pa.conv = p.conv_width == 4; pa.nch = plan.nchunks;

@@ -18,6 +18,10 @@ on: Qwen3.5-0.8B, Qwen3.5-4B and Qwen3.8-27B Gated DeltaNet layers):
 * initial recurrent state [B, Hv, 128, 128]: N(0, 0.1) fp32 (decode workload).
 * conv state [B, 3, Cc]: N(0, 1) -> bf16 (decode workload; stands in for the
   raw pre-conv activations it holds).
+* gate logits (make_gate_logits, for the calls that take them): a, b ~ N(0, 1)
+  fp32 [B, T, Hv]; A_log = ln(U(1, 16)) and dt_bias ~ U(-6.9, -2.3) fp32 per
+  value head (the usual initial ranges of these parameters: A in [1, 16], the
+  softplus of dt_bias in [1e-3, 0.1]).
 
 Every tensor is drawn in blocks of 2**24 elements; block ``j`` of tensor
 ``tid`` for workload tag ``tag`` uses
@@ -36,7 +40,8 @@ SEED_BASE = 20261202
 BLOCK = 1 << 24
 D = 128  # key and value head width of every shape here
 
-TID = dict(q=0, k=1, v=2, z=3, g=4, beta=5, conv_w=6, norm_w=7, state=8, conv_state=9)
+TID = dict(q=0, k=1, v=2, z=3, g=4, beta=5, conv_w=6, norm_w=7, state=8, conv_state=9,
+           gate_a=10, gate_b=11, A_log=12, dt_bias=13)
 
 
 @dataclass(frozen=True)
@@ -112,6 +117,12 @@ def _draw(n: int, tag: int, tid: int, kind: str, out_dtype) -> np.ndarray:
         elif kind == "logdecay_f32":
             u = g.uniform(0.8, 0.999, m)  # fp64
             out[lo:hi] = np.log(u).astype(np.float32)
+        elif kind == "normal_f32":
+            out[lo:hi] = g.standard_normal(m, dtype=np.float32)
+        elif kind == "alog_f32":
+            out[lo:hi] = np.log(g.uniform(1.0, 16.0, m)).astype(np.float32)
+        elif kind == "dtbias_f32":
+            out[lo:hi] = g.uniform(-6.9, -2.3, m).astype(np.float32)
         elif kind == "beta_f32":
             x = g.standard_normal(m)  # fp64
             out[lo:hi] = (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
@@ -153,3 +164,15 @@ def make_inputs(w: Workload) -> dict:
                        if (w.random_conv_state and w.conv) else None),
     }
     return out
+
+
+def make_gate_logits(w: Workload) -> dict:
+    """Gate inputs of workload ``w`` for the calls that take the raw logits: a, b
+    [B,T,Hv] fp32 and A_log, dt_bias [Hv] fp32 (see the module docstring)."""
+    B, T, Hv, t = w.B, w.T, w.Hv, w.tag
+    return {
+        "a": _draw(B * T * Hv, t, TID["gate_a"], "normal_f32", np.float32).reshape(B, T, Hv),
+        "b": _draw(B * T * Hv, t, TID["gate_b"], "normal_f32", np.float32).reshape(B, T, Hv),
+        "A_log": _draw(Hv, t, TID["A_log"], "alog_f32", np.float32),
+        "dt_bias": _draw(Hv, t, TID["dt_bias"], "dtbias_f32", np.float32),
+    }

@@ -57,6 +57,15 @@ class Prefill:
                         d["norm_w"], d["state_in"], d["conv_state_in"], self.o, self.state_out,
                         self.conv_state_out, self.ws, self.ws_bytes, stream=stream)
 
+    def run_gate_logits(self, gl: dict, stream=None):
+        """The same call through gdn_prefill_gate_logits; gl holds a, b, A_log, dt_bias
+        as numpy arrays or device tensors (g and beta of the inputs are not used)."""
+        t = {n: (x if isinstance(x, torch.Tensor) else to_dev(x)) for n, x in gl.items()}
+        d = self.d
+        gdn.gdn_prefill_gate_logits(self.shape, d["q"], d["k"], d["v"], t["a"], t["b"], t["A_log"], t["dt_bias"],
+                                    d["z"], d["conv_w"], d["norm_w"], d["state_in"], d["conv_state_in"], self.o,
+                                    self.state_out, self.conv_state_out, self.ws, self.ws_bytes, stream=stream)
+
     def exchange_error_word(self) -> int:
         """Last 32-bit word area of the workspace: non-zero if a bounded wait timed out."""
         return int(self.ws[-256:-252].view(torch.int32).item())
@@ -83,3 +92,11 @@ class Decode:
         d = self.d
         gdn.gdn_decode_step(self.shape, d["q"], d["k"], d["v"], d["g"], d["beta"], d["z"], d["conv_w"],
                             d["norm_w"], self.state, self.conv_state, self.o, stream=stream)
+
+    def run_gate_logits(self, gl: dict, stream=None):
+        """The step through gdn_decode_step_gate_logits (gl: a, b [B,Hv], A_log, dt_bias [Hv])."""
+        t = {n: (x if isinstance(x, torch.Tensor) else to_dev(x)) for n, x in gl.items()}
+        d = self.d
+        gdn.gdn_decode_step_gate_logits(self.shape, d["q"], d["k"], d["v"], t["a"], t["b"], t["A_log"],
+                                        t["dt_bias"], d["z"], d["conv_w"], d["norm_w"], self.state,
+                                        self.conv_state, self.o, stream=stream)

@@ -26,7 +26,9 @@
  * Conventions for every call.
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous; bf16
  *    tensors are passed as uint16_t bit patterns.  The caller owns every
- *    buffer.  The library allocates nothing and never synchronises.
+ *    buffer.  The library allocates no device memory and never synchronises
+ *    (the first prefill on a device creates one side stream and two events,
+ *    kept until the process ends; see gdn_prefill).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it; results are visible once the caller syncs it.
  *  - Every argument is checked on the host before any HIP call; a failed
@@ -143,6 +145,32 @@ int gdn_decode_step(const gdn_shape *shape, const uint16_t *q, const uint16_t *k
                     const uint16_t *v, const float *g, const float *beta, const uint16_t *z,
                     const uint16_t *conv_w, const uint16_t *norm_w, float *state,
                     uint16_t *conv_state, uint16_t *o, void *stream);
+
+/*
+ * The same two calls taking the raw gate inputs in place of g and beta ("How
+ * Qwen3.5 works" §9.5: beta_t = sigmoid(b_t) and g_t = -exp(A_log)
+ * softplus(a_t + dt_bias), per value head, computed in fp32 inside the kernels):
+ *
+ *  a, b      gate logits, fp32, laid out as g and beta ([B][T][Hv] for prefill,
+ *            [B][Hv] for decode); 4-byte aligned
+ *  A_log     [Hv] fp32 per value head (alpha_t = exp(g_t) multiplies the state)
+ *  dt_bias   [Hv] fp32 per value head
+ *
+ * Every other argument, check and status is that of gdn_prefill or
+ * gdn_decode_step; the four gate arrays count as inputs for the aliasing checks.
+ */
+int gdn_prefill_gate_logits(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const float *a, const float *b, const float *A_log,
+                            const float *dt_bias, const uint16_t *z, const uint16_t *conv_w,
+                            const uint16_t *norm_w, const float *state_in,
+                            const uint16_t *conv_state_in, uint16_t *o, float *state_out,
+                            uint16_t *conv_state_out, void *workspace, size_t workspace_bytes,
+                            void *stream);
+int gdn_decode_step_gate_logits(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
+                                const uint16_t *v, const float *a, const float *b,
+                                const float *A_log, const float *dt_bias, const uint16_t *z,
+                                const uint16_t *conv_w, const uint16_t *norm_w, float *state,
+                                uint16_t *conv_state, uint16_t *o, void *stream);
 
 /* A static, NUL-terminated description of a status code. */
 const char *gdn_status_string(int status);

@@ -25,6 +25,8 @@
  *        silu(z), eps = 1e-6.
  *  [AD]  Qwen3.5-4B architecture page (ayushdeva.com), delta-rule derivation
  *        and the d = 2 single-head walkthrough.
+ *  [HQ]  §9.5 the gates from their logits: beta = sigmoid(b),
+ *        g = -exp(A_log) softplus(a + dt_bias), alpha = exp(g).
  *
  * Memory orientation: the state is stored K-major, S[i][j] with i a key
  * dimension and j a value dimension ([HQ] §9.1 orientation S in R^{dk x dv},
@@ -91,6 +93,25 @@ void oracle_l2norm(int n, const double *x, double eps, double scale, double *out
     double inv = scale / sqrt(ss + eps);
     for (int i = 0; i < n; ++i)
         out[i] = x[i] * inv;
+}
+
+/*
+ * The gates from their logits, [HQ] §9.5: for n tokens of Hv value heads (a, b
+ * laid out [n][Hv], A_log and dt_bias per head),
+ *   beta = sigmoid(b) = 1 / (1 + e^{-b}),
+ *   g    = -exp(A_log[h]) * softplus(a + dt_bias[h]),  softplus(x) = ln(1 + e^x)
+ * (ln(1 + e^x) evaluated as x + ln(1 + e^{-x}) for x > 0 so e^x cannot overflow).
+ */
+void oracle_gate_logits(int n, int Hv, const double *a, const double *b, const double *A_log,
+                        const double *dt_bias, double *g, double *beta)
+{
+    for (int t = 0; t < n; ++t)
+        for (int h = 0; h < Hv; ++h) {
+            const double x = a[(size_t)t * Hv + h] + dt_bias[h];
+            const double sp = x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+            g[(size_t)t * Hv + h] = -exp(A_log[h]) * sp;
+            beta[(size_t)t * Hv + h] = 1.0 / (1.0 + exp(-b[(size_t)t * Hv + h]));
+        }
 }
 
 /* Gated RMSNorm of one head vector ([FE] gdn.norm, [HQ] §9.9):

@@ -57,6 +57,8 @@ def load():
     lib.oracle_l2norm.restype = None
     lib.oracle_gated_rmsnorm.argtypes = [C.c_int, _d, _d, _d, C.c_double, _d]
     lib.oracle_gated_rmsnorm.restype = None
+    lib.oracle_gate_logits.argtypes = [C.c_int, C.c_int, _d, _d, _d, _d, _d, _d]
+    lib.oracle_gate_logits.restype = None
     lib.oracle_prefill.argtypes = [C.c_int] * 8 + [C.c_double, C.c_double] + [
         _u16, _u16, _u16, _f32, _f32, _u16, _u16, _u16, _f32, _u16, C.c_int, _i32, _d, _d, _u16, C.c_int]
     lib.oracle_num_threads.argtypes = []
@@ -127,6 +129,19 @@ def gated_rmsnorm(o, z, w, eps=1e-6):
     y = np.zeros_like(o)
     load().oracle_gated_rmsnorm(len(o), _p(o, _d), _p(z, _d), _p(w, _d), eps, _p(y, _d))
     return y
+
+
+def gate_logits(a, b, A_log, dt_bias):
+    """g and beta from the gate logits ("How Qwen3.5 works" §9.5), fp64.  a, b have
+    the value head as their last axis; A_log, dt_bias are per value head."""
+    lib = load()
+    a64, b64 = _f64(a), _f64(b)
+    Hv = a64.shape[-1]
+    g = np.empty_like(a64)
+    beta = np.empty_like(a64)
+    lib.oracle_gate_logits(a64.size // Hv, Hv, _p(a64, _d), _p(b64, _d), _p(_f64(A_log), _d),
+                           _p(_f64(dt_bias), _d), _p(g, _d), _p(beta, _d))
+    return g, beta
 
 
 def prefill(inp: dict, B: int, T: int, Hk: int, Hv: int, conv: bool, norm: bool,

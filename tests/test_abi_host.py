@@ -24,8 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
-        ["gdn_decode_step", "gdn_last_error", "gdn_prefill", "gdn_prefill_workspace_size", "gdn_state_init",
-         "gdn_status_string"])
+        ["gdn_decode_step", "gdn_decode_step_gate_logits", "gdn_last_error", "gdn_prefill",
+         "gdn_prefill_gate_logits", "gdn_prefill_workspace_size", "gdn_state_init", "gdn_status_string"])
 
 
 def test_last_error_is_a_string_before_any_failure():
@@ -153,6 +153,34 @@ def test_decode_rejects_bad_arguments():
     assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
     s2 = _shape(Hk=1, Hv=65)
     assert f(C.byref(s2), *ok, None) == gdn.GDN_EUNSUPPORTED
+
+
+def _call_prefill_logits(shape, A_log, dt_bias, **over):
+    a = _prefill_args(shape, **over)
+    return gdn._lib.gdn_prefill_gate_logits(
+        C.byref(shape), a["q"], a["k"], a["v"], a["g"], a["beta"], A_log, dt_bias, a["z"], a["conv_w"],
+        a["norm_w"], a["state_in"], a["conv_state_in"], a["o"], a["state_out"], a["conv_state_out"],
+        a["workspace"], a["workspace_bytes"], None)
+
+
+def test_gate_logit_entry_points_reject_bad_arguments():
+    s = _shape()
+    a = _prefill_args(s)
+    gates = a["workspace"] + (1 << 34)          # two fp32 [Hv] arrays far from everything else
+    assert _call_prefill_logits(s, None, gates) == gdn.GDN_EINVAL
+    assert _call_prefill_logits(s, gates, None) == gdn.GDN_EINVAL
+    assert _call_prefill_logits(s, gates + 2, gates + 1024) == gdn.GDN_EINVAL   # 4-byte alignment
+    assert _call_prefill_logits(s, a["o"], gates) == gdn.GDN_EINVAL             # A_log inside o
+    assert _call_prefill_logits(s, gates, a["workspace"]) == gdn.GDN_EINVAL     # dt_bias inside the workspace
+    assert _call_prefill_logits(s, gates, gates + 1024, q=None) == gdn.GDN_EINVAL
+    ok = [FAKE + i * (64 * MB) for i in range(13)]  # q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state, conv_state, o
+    f = gdn._lib.gdn_decode_step_gate_logits
+    bad = list(ok)
+    bad[5] = None
+    assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
+    bad = list(ok)
+    bad[6] = ok[12]  # dt_bias inside o
+    assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
 
 
 def test_state_init_rejects_bad_arguments():

@@ -34,6 +34,14 @@ MUTANTS = {
     "sigmoid_for_silu": ("static double silu(double x) { return x / (1.0 + exp(-x)); }",
                          "static double silu(double x) { return 1.0 / (1.0 + exp(-x)); }"),
     "norm_mean_over_sum": ("    ms /= (double)n;\n", "\n"),
+    "gate_a_log_not_exponentiated": ("g[(size_t)t * Hv + h] = -exp(A_log[h]) * sp;",
+                                     "g[(size_t)t * Hv + h] = -A_log[h] * sp;"),
+    "gate_beta_wrong_sign": ("beta[(size_t)t * Hv + h] = 1.0 / (1.0 + exp(-b[(size_t)t * Hv + h]));",
+                             "beta[(size_t)t * Hv + h] = 1.0 / (1.0 + exp(b[(size_t)t * Hv + h]));"),
+    "gate_dt_bias_dropped": ("const double x = a[(size_t)t * Hv + h] + dt_bias[h];",
+                             "const double x = a[(size_t)t * Hv + h];"),
+    "gate_softplus_without_log": ("const double sp = x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));",
+                                  "const double sp = exp(x);"),
     "chunk_decay_not_relative": ("A[(size_t)i * n + j] = beta[t0 + i] * kk * exp(G[i] - G[j]);",
                                  "A[(size_t)i * n + j] = beta[t0 + i] * kk * exp(G[i]);"),
 }

@@ -327,3 +327,45 @@ def test_split_prefill_equals_whole(T1):
     np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, rtol=1e-5, atol=1e-6)
     np.testing.assert_allclose(S2, S, rtol=1e-5, atol=1e-6)
     np.testing.assert_array_equal(cs2, cs)
+
+
+# --- gates from their logits ("How Qwen3.5 works" §9.5) ---------------------------------------
+
+def _gates(a, b, A_log, dt_bias):
+    return O.gate_logits(np.asarray(a, float), np.asarray(b, float), np.asarray(A_log, float),
+                         np.asarray(dt_bias, float))
+
+
+def test_gates_at_zero_logits():
+    """softplus(0) = ln 2 and sigmoid(0) = 1/2, so g = -e^{A_log} ln 2."""
+    g, beta = _gates(np.zeros((3, 2)), np.zeros((3, 2)), [0.0, np.log(5.0)], [0.0, 0.0])
+    np.testing.assert_allclose(g[:, 0], -np.log(2.0), rtol=1e-15)
+    np.testing.assert_allclose(g[:, 1], -5.0 * np.log(2.0), rtol=1e-14)
+    np.testing.assert_allclose(beta, 0.5, rtol=1e-15)
+
+
+def test_gate_identities():
+    """softplus(x) - softplus(-x) = x; sigmoid(x) + sigmoid(-x) = 1; d softplus/dx = sigmoid;
+    A_log scales g by e^{A_log}; dt_bias shifts the decay logit."""
+    x = np.linspace(-12.0, 12.0, 49)[:, None]
+    gp, bp = _gates(x, x, [0.0], [0.0])
+    gm, bm = _gates(-x, -x, [0.0], [0.0])
+    np.testing.assert_allclose(-(gp - gm), x, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(bp + bm, 1.0, rtol=1e-15)
+    h = 1e-5
+    g1, _ = _gates(x + h, x, [0.0], [0.0])
+    g0, _ = _gates(x - h, x, [0.0], [0.0])
+    np.testing.assert_allclose(-(g1 - g0) / (2 * h), bp, rtol=1e-8, atol=1e-10)
+    g3, _ = _gates(x, x, [np.log(3.0)], [0.0])
+    np.testing.assert_allclose(g3, 3.0 * gp, rtol=1e-14)
+    gs, _ = _gates(x - 0.75, x, [0.0], [0.75])
+    np.testing.assert_allclose(gs, gp, rtol=1e-12)
+
+
+def test_gate_extremes():
+    """Large decay logits: softplus(x) -> x; very negative ones: softplus(x) -> e^x (no decay)."""
+    g, beta = _gates([[50.0, -50.0]], [[40.0, -40.0]], [0.0, 0.0], [0.0, 0.0])
+    assert g[0, 0] == pytest.approx(-50.0, rel=1e-15)
+    assert g[0, 1] == pytest.approx(-np.exp(-50.0), rel=1e-12)
+    assert beta[0, 0] == pytest.approx(1.0, abs=1e-15) and beta[0, 1] == pytest.approx(np.exp(-40.0), rel=1e-12)
+    assert np.all(np.isfinite(_gates([[1e4]], [[-1e4]], [0.0], [0.0])[0]))
