@@ -21,6 +21,7 @@ GDN_EUNSUPPORTED = -2
 GDN_EHIP = -3
 GDN_EWORKSPACE = -4
 GDN_NO_NORM = 1
+GDN_PACKED = 2
 
 
 class GdnError(RuntimeError):
@@ -39,8 +40,11 @@ class gdn_shape(C.Structure):
 
 
 def make_shape(B: int, T: int, Hk: int, Hv: int, conv: bool = True, norm: bool = True,
-               eps_l2: float = 1e-6, eps_norm: float = 1e-6, Dk: int = 128, Dv: int = 128) -> gdn_shape:
-    return gdn_shape(B, T, Hk, Hv, Dk, Dv, 4 if conv else 0, 0 if norm else GDN_NO_NORM, eps_l2, eps_norm)
+               eps_l2: float = 1e-6, eps_norm: float = 1e-6, Dk: int = 128, Dv: int = 128,
+               packed: bool = False) -> gdn_shape:
+    """packed: B sequences of T tokens in all (gdn_prefill_packed)."""
+    flags = (0 if norm else GDN_NO_NORM) | (GDN_PACKED if packed else 0)
+    return gdn_shape(B, T, Hk, Hv, Dk, Dv, 4 if conv else 0, flags, eps_l2, eps_norm)
 
 
 # torch ships its own copy of the HIP runtime under the same soname.  Loading
@@ -66,9 +70,12 @@ _lib.gdn_prefill.argtypes = [_sp] + [_vp] * 14 + [C.c_size_t, _vp]
 _lib.gdn_decode_step.argtypes = [_sp] + [_vp] * 12
 _lib.gdn_prefill_gate_logits.argtypes = [_sp] + [_vp] * 16 + [C.c_size_t, _vp]
 _lib.gdn_decode_step_gate_logits.argtypes = [_sp] + [_vp] * 14
+_lib.gdn_prefill_packed.argtypes = [_sp] + [_vp] * 15 + [C.c_size_t, _vp]
+_lib.gdn_prefill_packed_gate_logits.argtypes = [_sp] + [_vp] * 17 + [C.c_size_t, _vp]
 
 EXPORTED = ("gdn_state_init", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
-            "gdn_prefill_gate_logits", "gdn_decode_step_gate_logits", "gdn_status_string", "gdn_last_error")
+            "gdn_prefill_gate_logits", "gdn_decode_step_gate_logits", "gdn_prefill_packed",
+            "gdn_prefill_packed_gate_logits", "gdn_status_string", "gdn_last_error")
 
 
 def _ptr(t):
@@ -147,3 +154,28 @@ def gdn_decode_step_gate_logits(shape: gdn_shape, q, k, v, a, b, A_log, dt_bias,
                                           _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(conv_w), _ptr(norm_w),
                                           _ptr(state), _ptr(conv_state), _ptr(o), _stream(stream))
     _check("gdn_decode_step_gate_logits", rc)
+
+
+def gdn_prefill_packed(shape: gdn_shape, cu_seqlens, q, k, v, g, beta, z, conv_w, norm_w, state_in,
+                       conv_state_in, o, state_out, conv_state_out, workspace,
+                       workspace_bytes: int | None = None, stream=None) -> None:
+    """cu_seqlens: int32 device tensor [B + 1]; the shape from make_shape(..., packed=True)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.gdn_prefill_packed(C.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                 _ptr(beta), _ptr(z), _ptr(conv_w), _ptr(norm_w), _ptr(state_in),
+                                 _ptr(conv_state_in), _ptr(o), _ptr(state_out), _ptr(conv_state_out),
+                                 _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("gdn_prefill_packed", rc)
+
+
+def gdn_prefill_packed_gate_logits(shape: gdn_shape, cu_seqlens, q, k, v, a, b, A_log, dt_bias, z, conv_w,
+                                   norm_w, state_in, conv_state_in, o, state_out, conv_state_out, workspace,
+                                   workspace_bytes: int | None = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.gdn_prefill_packed_gate_logits(
+        C.byref(shape), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+        _ptr(dt_bias), _ptr(z), _ptr(conv_w), _ptr(norm_w), _ptr(state_in), _ptr(conv_state_in), _ptr(o),
+        _ptr(state_out), _ptr(conv_state_out), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("gdn_prefill_packed_gate_logits", rc)

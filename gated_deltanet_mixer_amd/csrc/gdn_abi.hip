@@ -34,7 +34,7 @@ int check_shape(const gdn_shape *s, bool use_T) {
     if (s->Hv % s->Hk != 0) return GDN_EINVAL;
     if (s->Dk != kD || s->Dv != kD) return GDN_EUNSUPPORTED;
     if (s->conv_width != 0 && s->conv_width != 4) return GDN_EUNSUPPORTED;
-    if (s->flags & ~GDN_NO_NORM) return GDN_EINVAL;
+    if (s->flags & ~(GDN_NO_NORM | GDN_PACKED)) return GDN_EINVAL;
     if (!(s->eps_l2 >= 0.0f) || !(s->eps_norm >= 0.0f)) return GDN_EINVAL;
     // sizes must fit the kernels' 32-bit token and head indices
     if ((long long)s->B * s->Hv * kD > 0x7fffffffLL || (use_T && (long long)s->T * kD > 0x7fffffffLL))
@@ -78,7 +78,8 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes) {
     if (rc) return rc;
     if (!bytes) return GDN_EINVAL;
     PrefillPlan plan;
-    plan_prefill(shape->B, shape->T, shape->Hk, shape->Hv, &plan);
+    plan_prefill(shape->B, shape->T, shape->Hk, shape->Hv, (shape->flags & GDN_PACKED) != 0, &plan);
+    if (plan.nslots * shape->Hk > 0x7fffffffLL) return GDN_EINVAL;
     *bytes = plan.total_bytes;
     return GDN_OK;
 }
@@ -87,14 +88,18 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes) {
 
 namespace {
 
-// g, beta are the gate logits a, b when A_log and dt_bias are given (both or neither).
-int prefill_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+// g, beta are the gate logits a, b when A_log and dt_bias are given (both or neither);
+// cu_seqlens is given exactly when the shape carries GDN_PACKED.
+int prefill_impl(const gdn_shape *s, const int32_t *cu_seqlens, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                  const float *beta, const float *A_log, const float *dt_bias, const uint16_t *z,
                  const uint16_t *conv_w, const uint16_t *norm_w, const float *state_in,
                  const uint16_t *conv_state_in, uint16_t *o, float *state_out, uint16_t *conv_state_out,
                  void *workspace, size_t workspace_bytes, void *stream) {
     int rc = check_shape(s, true);
     if (rc) return rc;
+    const bool packed = (s->flags & GDN_PACKED) != 0;
+    if (packed != (cu_seqlens != nullptr)) return GDN_EINVAL;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return GDN_EINVAL;
     if ((A_log == nullptr) != (dt_bias == nullptr)) return GDN_EINVAL;
     if (A_log && (!aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_EINVAL;
     const bool norm = !(s->flags & GDN_NO_NORM);
@@ -108,8 +113,9 @@ int prefill_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const
         if (p && !aligned(p, 16)) return GDN_EINVAL;
     if (!aligned(g, 4) || !aligned(beta, 4)) return GDN_EINVAL;
 
-    const size_t B = s->B, T = s->T, Hk = s->Hk, Hv = s->Hv, Cc = conv_channels(s);
-    const size_t nqk = B * T * Hk * kD * 2, nv = B * T * Hv * kD * 2, ngb = B * T * Hv * 4;
+    const size_t B = s->B, Hk = s->Hk, Hv = s->Hv, Cc = conv_channels(s);
+    const size_t rows = packed ? (size_t)s->T : B * s->T;  // token rows of q, k, v, z, g, beta and o
+    const size_t nqk = rows * Hk * kD * 2, nv = rows * Hv * kD * 2, ngb = rows * Hv * 4;
     const size_t nst = B * Hv * kD * kD * 4, ncs = B * 3 * Cc * 2;
     const size_t nw = conv ? Cc * 4 * 2 : 0, nn = norm ? kD * 2 : 0;
     const struct {
@@ -117,7 +123,7 @@ int prefill_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const
         size_t n;
     } inputs[] = {{q, nqk}, {k, nqk}, {v, nv}, {g, ngb}, {beta, ngb}, {norm ? z : nullptr, nv},
                   {conv_w, nw}, {norm_w, nn}, {state_in, nst}, {conv_state_in, ncs},
-                  {A_log, Hv * 4}, {dt_bias, Hv * 4}};
+                  {A_log, Hv * 4}, {dt_bias, Hv * 4}, {cu_seqlens, (B + 1) * 4}};
     for (const auto &in : inputs)
         if (overlap(o, nv, in.p, in.n) || overlap(workspace, workspace_bytes, in.p, in.n)) return GDN_EINVAL;
     if (overlap(conv_state_out, ncs, conv_state_in, ncs)) return GDN_EINVAL;
@@ -131,7 +137,8 @@ int prefill_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const
         return GDN_EINVAL;
 
     PrefillPlan plan;
-    plan_prefill(s->B, s->T, s->Hk, s->Hv, &plan);
+    plan_prefill(s->B, s->T, s->Hk, s->Hv, packed, &plan);
+    if (plan.nslots * s->Hk > 0x7fffffffLL) return GDN_EINVAL;
     if (workspace_bytes < plan.total_bytes) return GDN_EWORKSPACE;
 
     PrefillParams p;
@@ -139,6 +146,7 @@ int prefill_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const
     p.conv_state_in = conv_state_in; p.g = g; p.beta = beta; p.A_log = A_log; p.dt_bias = dt_bias;
     p.state_in = state_in;
     p.o = o; p.conv_state_out = conv_state_out; p.state_out = state_out; p.workspace = workspace;
+    p.cu_seqlens = cu_seqlens;
     p.B = s->B; p.T = s->T; p.Hk = s->Hk; p.Hv = s->Hv; p.conv_width = s->conv_width; p.norm = norm;
     p.eps_l2 = s->eps_l2; p.eps_norm = s->eps_norm;
     return launch_prefill(p, plan, static_cast<hipStream_t>(stream)) ? GDN_EHIP : GDN_OK;
@@ -150,6 +158,7 @@ int decode_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const 
                 void *stream) {
     int rc = check_shape(s, false);
     if (rc) return rc;
+    if (s->flags & GDN_PACKED) return GDN_EINVAL;  // one token per sequence: nothing to pack
     if ((A_log == nullptr) != (dt_bias == nullptr)) return GDN_EINVAL;
     if (A_log && (!aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_EINVAL;
     const bool norm = !(s->flags & GDN_NO_NORM);
@@ -195,8 +204,8 @@ int gdn_prefill(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const 
                 const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
                 const float *state_in, const uint16_t *conv_state_in, uint16_t *o, float *state_out,
                 uint16_t *conv_state_out, void *workspace, size_t workspace_bytes, void *stream) {
-    return prefill_impl(s, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state_in, conv_state_in, o,
-                        state_out, conv_state_out, workspace, workspace_bytes, stream);
+    return prefill_impl(s, nullptr, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state_in, conv_state_in,
+                        o, state_out, conv_state_out, workspace, workspace_bytes, stream);
 }
 
 int gdn_prefill_gate_logits(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -205,8 +214,30 @@ int gdn_prefill_gate_logits(const gdn_shape *s, const uint16_t *q, const uint16_
                             const float *state_in, const uint16_t *conv_state_in, uint16_t *o, float *state_out,
                             uint16_t *conv_state_out, void *workspace, size_t workspace_bytes, void *stream) {
     if (!A_log || !dt_bias) return GDN_EINVAL;
-    return prefill_impl(s, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state_in, conv_state_in, o, state_out,
-                        conv_state_out, workspace, workspace_bytes, stream);
+    return prefill_impl(s, nullptr, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state_in, conv_state_in, o,
+                        state_out, conv_state_out, workspace, workspace_bytes, stream);
+}
+
+int gdn_prefill_packed(const gdn_shape *s, const int32_t *cu_seqlens, const uint16_t *q, const uint16_t *k,
+                       const uint16_t *v, const float *g, const float *beta, const uint16_t *z,
+                       const uint16_t *conv_w, const uint16_t *norm_w, const float *state_in,
+                       const uint16_t *conv_state_in, uint16_t *o, float *state_out, uint16_t *conv_state_out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    if (!cu_seqlens) return GDN_EINVAL;
+    return prefill_impl(s, cu_seqlens, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state_in,
+                        conv_state_in, o, state_out, conv_state_out, workspace, workspace_bytes, stream);
+}
+
+int gdn_prefill_packed_gate_logits(const gdn_shape *s, const int32_t *cu_seqlens, const uint16_t *q,
+                                   const uint16_t *k, const uint16_t *v, const float *a, const float *b,
+                                   const float *A_log, const float *dt_bias, const uint16_t *z,
+                                   const uint16_t *conv_w, const uint16_t *norm_w, const float *state_in,
+                                   const uint16_t *conv_state_in, uint16_t *o, float *state_out,
+                                   uint16_t *conv_state_out, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+    if (!cu_seqlens || !A_log || !dt_bias) return GDN_EINVAL;
+    return prefill_impl(s, cu_seqlens, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state_in, conv_state_in,
+                        o, state_out, conv_state_out, workspace, workspace_bytes, stream);
 }
 
 int gdn_decode_step(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,

@@ -22,6 +22,7 @@ struct PrefillParams {
     uint16_t *o, *conv_state_out;
     float *state_out;
     void *workspace;
+    const int *cu_seqlens;  // packed sequences: [B + 1] token offsets into [T] rows; nullptr: B rows of T
     int B, T, Hk, Hv, conv_width, norm;
     float eps_l2, eps_norm;
 };
@@ -32,9 +33,10 @@ struct PrefillPlan {
     int bv;              // value columns per chain workgroup (16 * nt)
     int nslice;          // workgroups per (sequence, value head): 128 / bv
     int nchunks;         // ceil(T / 64)
-    size_t qk_bytes;     // per (sequence, chunk, key head): q^, k^ [64][128], k^T [128][64] fp16
-    size_t tp_bytes;     // per (sequence, chunk, value head): T diag(beta), P (lower blocks, fp16), decay vectors
-    size_t ready_bytes;  // per (sequence, chunk, key head): stamp of the call whose operands are written
+    long long nslots;    // chunk operand slots: B nchunks, or floor(T / 64) + B for packed sequences
+    size_t qk_bytes;     // per (slot, key head): q^, k^ [64][128], k^T [128][64] fp16
+    size_t tp_bytes;     // per (slot, value head): T diag(beta), P (lower blocks, fp16), decay vectors
+    size_t ready_bytes;  // per (slot, key head): stamp of the call whose operands are written
     size_t mbox_bytes;   // exchange area (tagged partial sums, counters, error word)
     size_t total_bytes;
 };
@@ -44,7 +46,7 @@ struct PrefillPlan {
 int fail(const char *what, hipError_t e);
 int fail(const char *what);
 
-int plan_prefill(int B, int T, int Hk, int Hv, PrefillPlan *plan);
+int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan);
 int launch_decode(const DecodeParams &p, hipStream_t stream);
 int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream);
 int launch_state_init(float *state, size_t n_state, uint16_t *conv_state, size_t n_conv,

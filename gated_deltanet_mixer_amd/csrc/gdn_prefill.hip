@@ -166,6 +166,45 @@ __device__ __forceinline__ half4 lds_tr16(const _Float16 *p) {
 // chunk_prep_kernel
 // ========================================================================
 
+// Where sequence b's tokens and chunk operands sit.  An even batch (cu == nullptr):
+// tokens b T .. b T + T - 1 and operand slots b nch .. b nch + nch - 1.  Packed
+// sequences: tokens cu[b] .. cu[b+1] - 1 and slots from floor(cu[b] / 64) + b on.
+// Those bases grow from one sequence to the next by at least the chunk count of
+// the earlier one, so the slot ranges never overlap and all of them lie below
+// floor(T / 64) + B, without a prefix sum over the chunk counts.  Chunks start at
+// each sequence's first token: the recurrent state and the conv window start
+// afresh at every sequence boundary.  A packed sequence whose bounds are not
+// 0 <= cu[b] < cu[b+1] <= T comes back with no chunks (and nothing is read or
+// written for it).
+struct SeqInfo {
+    size_t tok0;
+    int T, c0, nch;
+};
+__device__ __forceinline__ SeqInfo seq_info(const int *cu, int b, int T, int nch) {
+    if (!cu) return SeqInfo{(size_t)b * T, T, b * nch, nch};
+    const int t0 = cu[b], t1 = cu[b + 1];
+    if (!(0 <= t0 && t0 < t1 && t1 <= T)) return SeqInfo{0, 0, 0, 0};
+    return SeqInfo{(size_t)t0, t1 - t0, t0 / kC + b, (t1 - t0 + kC - 1) / kC};
+}
+
+// Packed sequences: the sequence whose slot range may hold slot gc, the last b
+// in [0, B) with floor(cu[b] / 64) + b <= gc (those bases increase with b).  A
+// 64-way search, one wave: every lane tests one candidate per round, so B <= 64
+// takes one round of loads and B <= 4096 two.  The result is wave-uniform.
+__device__ __forceinline__ int find_seq(const int *cu, int B, int gc, int lane) {
+    int lo = 0, n = B;  // the answer lies in [lo, lo + n)
+    while (n > 1) {
+        const int step = (n + 63) >> 6;
+        const int cand = lo + lane * step;
+        const bool le = lane * step < n && cu[cand] / kC + cand <= gc;
+        const unsigned long long m = __ballot(le);
+        const int j = m ? 63 - __clzll(m) : 0;
+        lo += j * step;
+        n = min(step, n - j * step);
+    }
+    return lo;
+}
+
 struct PrepArgs {
     const uint16_t *q, *k, *conv_w, *conv_state_in;
     const float *g, *beta;      // or the gate logits a, b when A_log is set
@@ -173,9 +212,10 @@ struct PrepArgs {
     uint16_t *conv_state_out;
     _Float16 *qkf;  // [B][nch][Hk][kQKF]
     _Float16 *tpf;  // [B][nch][Hv][kTPF]
-    unsigned int *ready;  // [B][nch][Hk]: call stamp once the block's operands are written
+    unsigned int *ready;  // [chunks][Hk]: call stamp once the block's operands are written
     unsigned int stamp;
-    int B, T, Hk, Hv, r, Cc, conv, nch;
+    const int *cu;                     // packed sequences: [B + 1] token offsets (nullptr: even batch)
+    int B, T, Hk, Hv, r, Cc, conv, nch;  // nch: chunks per sequence of an even batch
     float eps_l2;
 };
 
@@ -196,7 +236,7 @@ struct PrepLds {
     static size_t bytes(int r) { return sGr + 2 * 4 * (size_t)kC * r; }
 };
 
-// grid (nch * Hk, B), 256 threads
+// grid (slots * Hk), 256 threads: slot b nch + c of an even batch, else where seq_info places it
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_prep_kernel(PrepArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + PrepLds::sQ);
@@ -212,9 +252,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave bases stay scalar
     const int l16 = lane & 15, lq = lane >> 4;
-    // blocks in chunk-major order, so the sequential pass can start on the first
-    // chunks while later ones are still being prepared
-    const int c = blockIdx.x / a.Hk, kh = blockIdx.x % a.Hk, b = blockIdx.y;
+    // blocks in chunk-major order (chunk gc of all sequences, numbered sequence by
+    // sequence), so the sequential pass can start on the first chunks while later ones are
+    // still being prepared
+    const int gc = blockIdx.x / a.Hk, kh = blockIdx.x % a.Hk;
+    const int b = a.cu ? find_seq(a.cu, a.B, gc, lane) : gc / a.nch;
+    const SeqInfo si = seq_info(a.cu, b, a.T, a.nch);
+    const int c = gc - si.c0;
+    if (c < 0 || c >= si.nch) {
+        // a slot between two packed sequences' ranges (or of an invalid one): nothing to
+        // prepare; its stamp is still set, so that no wait on it can outlast this kernel
+        if (tid == 0)
+            __hip_atomic_store(a.ready + (size_t)gc * a.Hk + kh, a.stamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     const int tc0 = c * kC;
     float *sGr = reinterpret_cast<float *>(smem + PrepLds::sGr);
 
@@ -225,8 +276,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int i = tid + 256 * u, row = i / a.r, t = tc0 + row;
-        if (i < ngb && t < a.T) {
-            const size_t gi = ((size_t)b * a.T + t) * a.Hv + kh * a.r + i % a.r;
+        if (i < ngb && t < si.T) {
+            const size_t gi = (si.tok0 + t) * a.Hv + kh * a.r + i % a.r;
             g_ld[u] = a.g[gi];
             b_ld[u] = a.beta[gi];
         }
@@ -235,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int i = tid + 256 * u, h = kh * a.r + i % a.r;
-            if (i < ngb && tc0 + i / a.r < a.T) {
+            if (i < ngb && tc0 + i / a.r < si.T) {
                 g_ld[u] = gate_g(g_ld[u], a.A_log[h], a.dt_bias[h]);
                 b_ld[u] = gate_beta(b_ld[u]);
             }
@@ -253,8 +304,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         const int r0 = c > 0 ? tc0 - 3 : 0;
         const unsigned int rowb = (unsigned int)a.Hk * kD * 2;
         const __amdgpu_buffer_rsrc_t rs =
-            make_rsrc((m ? a.k : a.q) + ((size_t)b * a.T + r0) * a.Hk * kD + kh * kD,
-                      (unsigned int)(min(a.T, tc0 + kC) - r0) * rowb);
+            make_rsrc((m ? a.k : a.q) + (si.tok0 + r0) * a.Hk * kD + kh * kD,
+                      (unsigned int)(min(si.T, tc0 + kC) - r0) * rowb);
         uint4 xr[2][7];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -317,7 +368,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += uu[i][e] * uu[i][e];
                 ss = group_sum<16>(ss);
-                const bool valid = tc0 + tl0 + i < a.T;
+                const bool valid = tc0 + tl0 + i < si.T;
                 const float sc = valid ? qscale / sqrtf(ss + a.eps_l2) : 0.0f;  // rows past T are zero
                 half8 hv;
 #pragma unroll
@@ -328,11 +379,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         // raw q/k inputs of the last three tokens -> conv state out
         if (c == 0 && a.conv && a.conv_state_out && tid < 96) {
             const int s = tid >> 5, mm = (tid >> 4) & 1, cq = tid & 15;
-            const int tau = a.T - 3 + s;
+            const int tau = si.T - 3 + s;
             const int cc = mm * a.Hk * kD + kh * kD + cq * 8;
             uint4 raw = make_uint4(0, 0, 0, 0);
             if (tau >= 0)
-                raw = *reinterpret_cast<const uint4 *>((mm ? a.k : a.q) + (((size_t)b * a.T + tau) * a.Hk + kh) * kD + cq * 8);
+                raw = *reinterpret_cast<const uint4 *>((mm ? a.k : a.q) + ((si.tok0 + tau) * a.Hk + kh) * kD + cq * 8);
             else if (a.conv_state_in)
                 raw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + tau)) * a.Cc + cc);
             *reinterpret_cast<uint4 *>(a.conv_state_out + ((size_t)b * 3 + s) * a.Cc + cc) = raw;
@@ -348,10 +399,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
     for (int i = tid + 512; i < ngb; i += 256) {  // more than 8 value heads per key head
         const int row = i / a.r, t = tc0 + row;
-        const size_t gi = ((size_t)b * a.T + t) * a.Hv + kh * a.r + i % a.r;
+        const size_t gi = (si.tok0 + t) * a.Hv + kh * a.r + i % a.r;
         const int h = kh * a.r + i % a.r;
-        float gv = t < a.T ? a.g[gi] : 0.0f, bv = t < a.T ? a.beta[gi] : 0.0f;
-        if (a.A_log && t < a.T) {
+        float gv = t < si.T ? a.g[gi] : 0.0f, bv = t < si.T ? a.beta[gi] : 0.0f;
+        if (a.A_log && t < si.T) {
             gv = gate_g(gv, a.A_log[h], a.dt_bias[h]);
             bv = gate_beta(bv);
         }
@@ -362,7 +413,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
     // ---- 1b. q^ and k^ to the workspace as operand fragments
     {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qkf + (((size_t)b * a.nch + c) * a.Hk + kh) * kQKF, kQKF * 2);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qkf + ((size_t)gc * a.Hk + kh) * kQKF, kQKF * 2);
         for (int idx = tid; idx < 32 * 64; idx += 256) {
             const int f = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
             const _Float16 *M = f < 16 ? sQ : sK;
@@ -397,7 +448,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // ---- 3. per value head of this key head
     for (int hr = 0; hr < a.r; ++hr) {
         const int h = kh * a.r + hr;
-        const __amdgpu_buffer_rsrc_t rtp = make_rsrc(a.tpf + (((size_t)b * a.nch + c) * a.Hv + h) * kTPF, kTPF * 2);
+        const __amdgpu_buffer_rsrc_t rtp = make_rsrc(a.tpf + ((size_t)gc * a.Hv + h) * kTPF, kTPF * 2);
         if (wave == 0) {
             float gv = sGr[hr * kC + lane];
             const float bv = sGr[(a.r + hr) * kC + lane];
@@ -531,7 +582,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     wait_vmcnt<0>();
     __syncthreads();
     if (tid == 0)
-        __hip_atomic_store(a.ready + ((size_t)b * a.nch + c) * a.Hk + kh, a.stamp, __ATOMIC_RELAXED,
+        __hip_atomic_store(a.ready + (size_t)gc * a.Hk + kh, a.stamp, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -567,8 +618,9 @@ struct ChainArgs {
     unsigned int *err;
     unsigned int *tickets;     // [8] next item of each XCD queue
     unsigned int *exits;       // workgroups that have left the item loop
-    const unsigned int *ready; // [B][nch][Hk] prep stamps
+    const unsigned int *ready; // [slots][Hk] prep stamps
     unsigned int stamp;
+    const int *cu;             // packed sequences: [B + 1] token offsets (nullptr: even batch)
     int B, T, Hk, Hv, r, Cc, conv, norm, nch, n_items, grid;
     float eps_norm;
 };
@@ -776,20 +828,20 @@ __device__ __forceinline__ int mod3(int x) { return ((x % 3) + 3) % 3; }
 
 
 // The prep kernel may still be running while this one starts: prep block
-// (sequence b, chunk cc, key head kh) stores this call's stamp once its operands
+// (operand slot gc, key head kh) stores this call's stamp once its operands
 // are written back (agent-scope release).  A chunk's operands are first touched
 // after its stamp has been seen, and no cache of this kernel holds lines of them
 // from before (caches are invalidated when a kernel starts and nothing loads a
 // chunk early), so a relaxed load of the stamp suffices.
-__device__ __forceinline__ const unsigned int *ready_word(const ChainArgs &a, int b, int cc, int kh) {
-    return a.ready + ((size_t)b * a.nch + cc) * a.Hk + kh;
+__device__ __forceinline__ const unsigned int *ready_word(const ChainArgs &a, int gc, int kh) {
+    return a.ready + (size_t)gc * a.Hk + kh;
 }
 __device__ __forceinline__ bool stamp_ok(const ChainArgs &a, unsigned int w) { return (int)(w - a.stamp) >= 0; }
 
 // Wait until the prep block is complete.  Bounded like every cross-workgroup
 // wait: on a timeout the error word is raised.
-__device__ __forceinline__ void wait_ready(const ChainArgs &a, int b, int cc, int kh, int &broken) {
-    const unsigned int *f = ready_word(a, b, cc, kh);
+__device__ __forceinline__ void wait_ready(const ChainArgs &a, int gc, int kh, int &broken) {
+    const unsigned int *f = ready_word(a, gc, kh);
     uint32_t n = 0;
     while (!stamp_ok(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
         if (broken || ++n > kSpinLimit) {
@@ -882,13 +934,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (item < 0) break;
         const int chain = item / NSL, s = item % NSL;
         const int b = chain / a.Hv, h = chain % a.Hv, kh = h / a.r;
+        const SeqInfo si = seq_info(a.cu, b, a.T, a.nch);
+        const int nch = si.nch, sc0 = si.c0;
         const int sv0 = s * BV;
-        const int last = a.nch + 2 + kLag;
+        const int last = nch + 2 + kLag;
         const size_t qk_stride = (size_t)a.Hk * kQKF, tp_stride = (size_t)a.Hv * kTPF;
-        const _Float16 *qk0 = a.qkf + ((size_t)b * a.nch * a.Hk + kh) * kQKF;
-        const _Float16 *tp0 = a.tpf + ((size_t)b * a.nch * a.Hv + h) * kTPF;
+        const _Float16 *qk0 = a.qkf + ((size_t)sc0 * a.Hk + kh) * kQKF;
+        const _Float16 *tp0 = a.tpf + ((size_t)sc0 * a.Hv + h) * kTPF;
 
-        if (is_a) {
+        if (nch == 0) {
+            // a packed sequence with invalid bounds: flagged, nothing read or written
+            if (tid == 0) atomicOr(a.err, 2u);
+        } else if (is_a) {
             // ---------------------------------------------------------- state wave
             const int jc = 16 * wave + l16;
             // transposing-read lane offset (fp16 elements): row j = l16 / 4 of the 16-lane
@@ -896,7 +953,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // swizzled LDS position
             const int trofs = kswz((4 * lq + (l16 >> 2)) + 16 * (l16 & 3)) * 8;
             StateFrags fr;
-            wait_ready(a, b, 0, kh, broken);
+            wait_ready(a, sc0, kh, broken);
             state_load(fr, tp0, lane, lq);
             floatx4 S[8];
             {
@@ -910,8 +967,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             lds_barrier();
             lds_barrier();
             for (int c = 0; c <= last; ++c) {
-                if (c < a.nch)
-                    state_step<NT>(smem, S, fr, tp0 + min(c + 1, a.nch - 1) * tp_stride, c, wave, lane, jc, lq, trofs);
+                if (c < nch)
+                    state_step<NT>(smem, S, fr, tp0 + min(c + 1, nch - 1) * tp_stride, c, wave, lane, jc, lq, trofs);
                 lds_barrier();
             }
 #pragma unroll
@@ -923,14 +980,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // ---------------------------------------------------------- output wave
             const int t = wave - NT, jc = 16 * t + l16;
             OutFrags fr;
-            wait_ready(a, b, 0, kh, broken);
+            wait_ready(a, sc0, kh, broken);
             out_load(fr, qk0, tp0, lane, lq);
             lds_barrier();
             lds_barrier();
             for (int c = 0; c <= last; ++c) {
-                if (c >= 1 && c - 1 < a.nch) {
+                if (c >= 1 && c - 1 < nch) {
                     out_step<NT>(smem, fr, c - 1, t, lane, jc, lq);
-                    if (c < a.nch) out_load(fr, qk0 + c * qk_stride, tp0 + c * tp_stride, lane, lq);
+                    if (c < nch) out_load(fr, qk0 + c * qk_stride, tp0 + c * tp_stride, lane, lq);
                 }
                 lds_barrier();
             }
@@ -939,10 +996,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // raw v / z rows of chunk cc: a buffer from the chunk's first token, so rows past T read as 0;
             // lane -> row (64 / NRD rows per instruction), 8-column group
             auto rows_dma = [&](const uint16_t *x, int cc, uint16_t *dst) __attribute__((always_inline)) {
-                const int c0 = min(max(cc, 0), a.nch - 1) * kC;
-                const unsigned int nrow = (unsigned int)min(a.T - c0, kC);
+                const int c0 = min(max(cc, 0), nch - 1) * kC;
+                const unsigned int nrow = (unsigned int)min(si.T - c0, kC);
                 const __amdgpu_buffer_rsrc_t r =
-                    make_rsrc(x + ((size_t)b * a.T + c0) * a.Hv * kD, nrow * (unsigned int)a.Hv * kD * 2);
+                    make_rsrc(x + (si.tok0 + c0) * a.Hv * kD, nrow * (unsigned int)a.Hv * kD * 2);
 #pragma unroll
                 for (int u = 0; u < NRD; ++u) {
                     const int i = lane + 64 * u, row = i / NCG, cg = i % NCG;
@@ -950,7 +1007,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             };
             auto ops_dma = [&](int cc) __attribute__((always_inline)) {
-                const int cl = min(cc, a.nch - 1);  // (past the last chunk: a harmless duplicate)
+                const int cl = min(cc, nch - 1);  // (past the last chunk: a harmless duplicate)
                 unsigned char *slot = smem + L::sOp + (cc % kDma) * kOpSlot;
                 const _Float16 *kb = qk0 + cl * qk_stride + kKOff;
 #pragma unroll
@@ -960,16 +1017,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // prologue: operands of chunks 0 and 1, raw v of chunks 0..2.  The load wave is
             // the one that waits for the prep blocks: A and B load a chunk's operands only
             // after the barrier that follows its wait.
-            wait_ready(a, b, 0, kh, broken);
-            if (a.nch > 1) wait_ready(a, b, 1, kh, broken);
+            wait_ready(a, sc0, kh, broken);
+            if (nch > 1) wait_ready(a, sc0 + 1, kh, broken);
             ops_dma(0);
             ops_dma(1);
             // a chunk's stamp is requested two iterations before it is needed, so that waiting
-            // for the previous iteration's DMA group never waits for a stamp load as well
+            // for the previous iteration's DMA group never waits for a stamp load as well.  The
+            // load is issued in every iteration, past the last chunk from the last chunk's word
+            // (that value is never tested): the group wait below counts it, and a skipped load
+            // would let the previous group's last DMA still be in flight after the wait.
+            // (The word's offset gets a zero the compiler cannot see through: the value then counts
+            // as per-lane and stays in a vector register, which nothing waits for until the test.
+            // As a wave-uniform value it would be moved to a scalar register right after the load,
+            // and that move waits for every load in flight, the DMA groups included.)
+            int zero_v;
+            asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
             auto stamp_load = [&](int cc) __attribute__((always_inline)) {
-                return cc < a.nch ? __hip_atomic_load(ready_word(a, b, cc, kh), __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT)
-                                  : a.stamp;
+                return __hip_atomic_load(ready_word(a, sc0 + min(cc, nch - 1), kh) + zero_v, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
             };
             // two stamp registers used in turn (iteration c reads and refills the one of its
             // parity), so no in-flight load is ever copied between registers
@@ -985,7 +1050,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // group would make the wave wait for that whole group)
                 __builtin_amdgcn_sched_barrier(0);
                 // this iteration's group: operands of chunk c+2, raw v of chunk c+3, z of chunk c-1-kLag
-                if (c + 2 < a.nch && !stamp_ok(a, st)) wait_ready(a, b, c + 2, kh, broken);
+                if (c + 2 < nch && !stamp_ok(a, st)) wait_ready(a, sc0 + c + 2, kh, broken);
                 st = stamp_load(c + 4);
                 ops_dma(c + 2);
                 rows_dma(a.v, c + 3, sRawV + mod3(c + 3) * kC * BV);
@@ -1097,8 +1162,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                         for (int e = 0; e < 8; ++e) y[e] = nw[e] * (y[e] * rstd) * (zf[e] * t8[e]);
                     }
-                    if (tt < a.T)
-                        *reinterpret_cast<uint4 *>(a.o + (((size_t)b * a.T + tt) * a.Hv + h) * kD + sv0 + cgl * 8) =
+                    if (tt < si.T)
+                        *reinterpret_cast<uint4 *>(a.o + ((si.tok0 + tt) * a.Hv + h) * kD + sv0 + cgl * 8) =
                             pack_bf16x8(y);
                 }
             };
@@ -1118,7 +1183,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (vh == 0) {
                 unsigned long long mbn[NSL] = {};  // sibling words of chunk rc, requested an iteration early
                 auto mb_request = [&](int cc) __attribute__((always_inline)) {
-                    if (a.norm && cc >= 0 && cc < a.nch) {
+                    if (a.norm && cc >= 0 && cc < nch) {
 #pragma unroll
                         for (int sib = 0; sib < NSL; ++sib)
                             mbn[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + (cc % kRing)) * kC,
@@ -1130,7 +1195,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     // 1/rms of chunk rc from the siblings' words (published kLag - 1 iterations before
                     // they were requested; a word without the chunk's tag is waited for)
                     const int rc = c - 2 - kLag;
-                    if (a.norm && rc >= 0 && rc < a.nch) {
+                    if (a.norm && rc >= 0 && rc < nch) {
                         float tot = 0.0f;
 #pragma unroll
                         for (int sib = 0; sib < NSL; ++sib) {
@@ -1142,7 +1207,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         sRstd[(rc & 1) * kC + lane] = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.eps_norm);
                     }
                     // row sums of chunk c-2 over this slice's columns -> mailbox (tag c-1)
-                    if (a.norm && c >= 2 && c - 2 < a.nch) {
+                    if (a.norm && c >= 2 && c - 2 < nch) {
                         const float *src = sO + ((c - 2) % kORing) * VT + lane;
                         float ov[BV];
 #pragma unroll
@@ -1161,20 +1226,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             } else {
                 for (int c = 0; c <= last; ++c) {
-                    if (vtid >= kConvBase && c + 1 < a.nch) conv_v(c + 1);
+                    if (vtid >= kConvBase && c + 1 < nch) conv_v(c + 1);
                     const int oc = c - 3 - kLag;
-                    if (vtid < 64 + kGateLanes && oc >= 0 && oc < a.nch) gate(oc);
+                    if (vtid < 64 + kGateLanes && oc >= 0 && oc < nch) gate(oc);
                     lds_barrier();
                 }
             }
             // raw v inputs of the last three tokens -> conv state out
             if (vh == 0 && a.conv && a.conv_state_out && lane < 3 * NCG) {
                 const int sidx = lane / NCG, cg = lane % NCG;
-                const int tau = a.T - 3 + sidx;
+                const int tau = si.T - 3 + sidx;
                 const int ch = 2 * a.Hk * kD + h * kD + sv0 + cg * 8;
                 uint4 rw = make_uint4(0, 0, 0, 0);
                 if (tau >= 0)
-                    rw = *reinterpret_cast<const uint4 *>(a.v + (((size_t)b * a.T + tau) * a.Hv + h) * kD + sv0 + cg * 8);
+                    rw = *reinterpret_cast<const uint4 *>(a.v + ((si.tok0 + tau) * a.Hv + h) * kD + sv0 + cg * 8);
                 else if (a.conv_state_in)
                     rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + tau)) * a.Cc + ch);
                 *reinterpret_cast<uint4 *>(a.conv_state_out + ((size_t)b * 3 + sidx) * a.Cc + ch) = rw;
@@ -1258,16 +1323,18 @@ int chain_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
 
 } // namespace
 
-int plan_prefill(int B, int T, int Hk, int Hv, PrefillPlan *plan) {
+int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan) {
     const long long chains = (long long)B * Hv;
     const int nsl = chains <= 32 ? 8 : 4;
     plan->nslice = nsl;
     plan->nt = kTiles / nsl;
     plan->bv = 16 * plan->nt;
     plan->nchunks = (T + kC - 1) / kC;
-    plan->qk_bytes = align256((size_t)B * plan->nchunks * Hk * kQKF * sizeof(_Float16));
-    plan->tp_bytes = align256((size_t)B * plan->nchunks * Hv * kTPF * sizeof(_Float16));
-    plan->ready_bytes = align256((size_t)B * plan->nchunks * Hk * sizeof(unsigned int));
+    // packed: sequence b's chunks from slot floor(cu[b] / 64) + b on, all below floor(T / 64) + B
+    plan->nslots = packed ? (long long)(T / kC) + B : (long long)B * plan->nchunks;
+    plan->qk_bytes = align256((size_t)plan->nslots * Hk * kQKF * sizeof(_Float16));
+    plan->tp_bytes = align256((size_t)plan->nslots * Hv * kTPF * sizeof(_Float16));
+    plan->ready_bytes = align256((size_t)plan->nslots * Hk * sizeof(unsigned int));
     plan->mbox_bytes = align256((size_t)chains * kTiles * kRing * kC * sizeof(unsigned long long)) +
                        align256((size_t)chains * sizeof(unsigned int)) + 256;
     plan->total_bytes = plan->qk_bytes + plan->tp_bytes + plan->ready_bytes + plan->mbox_bytes;
@@ -1338,7 +1405,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     PrepArgs pa;
     pa.q = p.q; pa.k = p.k; pa.conv_w = p.conv_w; pa.conv_state_in = p.conv_state_in;
     pa.g = p.g; pa.beta = p.beta; pa.A_log = p.A_log; pa.dt_bias = p.dt_bias; pa.conv_state_out = p.conv_state_out;
-    pa.qkf = qkf; pa.tpf = tpf; pa.ready = ready; pa.stamp = stamp;
+    pa.qkf = qkf; pa.tpf = tpf; pa.ready = ready; pa.stamp = stamp; pa.cu = p.cu_seqlens;
     pa.B = p.B; pa.T = p.T; pa.Hk = p.Hk; pa.Hv = p.Hv; pa.r = p.Hv / p.Hk;
     pa.Cc = 2 * p.Hk * kD + p.Hv * kD; pa.conv = p.conv_width == 4; pa.nch = plan.nchunks;
     pa.eps_l2 = p.eps_l2;
@@ -1348,7 +1415,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w; a.conv_state_in = p.conv_state_in;
     a.state_in = p.state_in; a.o = p.o; a.conv_state_out = p.conv_state_out; a.state_out = p.state_out;
     a.mbox = reinterpret_cast<unsigned long long *>(mb); a.counters = counters; a.err = err;
-    a.tickets = err + 16; a.exits = err + 32; a.ready = ready; a.stamp = stamp;
+    a.tickets = err + 16; a.exits = err + 32; a.ready = ready; a.stamp = stamp; a.cu = p.cu_seqlens;
     a.B = p.B; a.T = p.T; a.Hk = p.Hk; a.Hv = p.Hv; a.r = pa.r; a.Cc = pa.Cc; a.conv = pa.conv; a.norm = p.norm;
     a.nch = plan.nchunks; a.n_items = (int)(chains * plan.nslice); a.grid = 0;
     a.eps_norm = p.eps_norm;
@@ -1388,7 +1455,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
         return fail("hipFuncSetAttribute(chunk_prep_kernel)", e);
     void *pargs[] = {&pa};
     if ((e = hipLaunchKernel(reinterpret_cast<const void *>(chunk_prep_kernel),
-                             dim3((unsigned)(plan.nchunks * p.Hk), (unsigned)p.B), dim3(256), pargs, plds, ps)) !=
+                             dim3((unsigned)(plan.nslots * p.Hk)), dim3(256), pargs, plds, ps)) !=
         hipSuccess)
         return fail("hipLaunchKernel(chunk_prep_kernel)", e);
     if (beside && (e = hipEventRecord(ss->done, ps)) != hipSuccess) return fail("hipEventRecord", e);

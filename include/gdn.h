@@ -57,6 +57,7 @@ extern "C" {
 
 /* flags */
 #define GDN_NO_NORM 1u /* return the raw read-out o instead of the gated RMSNorm (z, norm_w unused) */
+#define GDN_PACKED 2u  /* packed sequences: B sequences of different lengths, T tokens in all (gdn_prefill_packed) */
 
 typedef struct gdn_shape {
     int32_t B;          /* sequences, >= 1 */
@@ -66,7 +67,7 @@ typedef struct gdn_shape {
     int32_t Dk;         /* key head width: must be 128 */
     int32_t Dv;         /* value head width: must be 128 */
     int32_t conv_width; /* 0: q, k, v enter the rule as given (no conv, no SiLU); 4: width-4 causal conv + SiLU */
-    uint32_t flags;     /* GDN_NO_NORM or 0 */
+    uint32_t flags;     /* GDN_NO_NORM, GDN_PACKED (prefill only), both or 0 */
     float eps_l2;       /* eps inside the q/k L2-norm root (1e-6 on the pages) */
     float eps_norm;     /* eps of the gated RMSNorm (1e-6 on the pages) */
 } gdn_shape;
@@ -80,7 +81,8 @@ typedef struct gdn_shape {
 int gdn_state_init(const gdn_shape *shape, float *state, uint16_t *conv_state, void *stream);
 
 /*
- * Bytes of device workspace gdn_prefill needs for `shape` (written to *bytes).
+ * Bytes of device workspace gdn_prefill (gdn_prefill_packed, when the shape
+ * carries GDN_PACKED) needs for `shape` (written to *bytes).
  * The workspace holds the state-independent chunk operands that one kernel
  * computes for the sequential pass of another: the normalised q/k rows (fp16,
  * B*T*Hk*2*Dk values), per (chunk, value head) the packed lower-triangular
@@ -171,6 +173,51 @@ int gdn_decode_step_gate_logits(const gdn_shape *shape, const uint16_t *q, const
                                 const float *A_log, const float *dt_bias, const uint16_t *z,
                                 const uint16_t *conv_w, const uint16_t *norm_w, float *state,
                                 uint16_t *conv_state, uint16_t *o, void *stream);
+
+/*
+ * Prefill over packed sequences of different lengths, one call for the whole
+ * batch.  The shape carries GDN_PACKED; B is the number of sequences and T the
+ * number of tokens of all of them together.  Sequence b owns the token rows
+ * cu_seqlens[b] .. cu_seqlens[b+1] - 1 of the token-major tensors; its
+ * recurrent state and conv window start from its own state_in / conv_state_in
+ * entries at its first token and end in its own state_out / conv_state_out
+ * entries, exactly as if it had been run alone through gdn_prefill with
+ * B = 1, T = its length ("How Qwen3.5 works" §12.2: when several samples are
+ * packed into one sequence, the conv and recurrent states must stop at every
+ * sample boundary, and a packed run must agree with the samples run one by
+ * one).  Chunks of 64 tokens start at each sequence's first token.
+ *
+ *  cu_seqlens     [B + 1] int32, DEVICE memory, 4-byte aligned: cu_seqlens[0] = 0,
+ *                 cu_seqlens[B] = T, every sequence at least one token long
+ *                 (cu_seqlens[b] < cu_seqlens[b+1]).  Read by the kernels, so the
+ *                 call does not synchronise; a sequence whose bounds break this
+ *                 rule is skipped (nothing of it is read or written, its outputs
+ *                 keep their contents) and every other sequence is still computed.
+ *  q, k           [T][Hk][128] bf16 (token-major over the packed batch)
+ *  v, z, o        [T][Hv][128] bf16
+ *  g, beta        [T][Hv] fp32
+ *  state_in/out   [B][Hv][128][128] fp32;  conv_state_in/out [B][3][Cc] bf16
+ *
+ * gdn_prefill_workspace_size() with the same shape (GDN_PACKED set) gives the
+ * workspace, which follows the rules of gdn_prefill.  Every other argument,
+ * check and status is that of gdn_prefill (or, for the _gate_logits variant,
+ * of gdn_prefill_gate_logits); cu_seqlens counts as an input for the aliasing
+ * checks.  gdn_prefill rejects a shape with GDN_PACKED, these two one without.
+ */
+int gdn_prefill_packed(const gdn_shape *shape, const int32_t *cu_seqlens, const uint16_t *q,
+                       const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                       const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
+                       const float *state_in, const uint16_t *conv_state_in, uint16_t *o,
+                       float *state_out, uint16_t *conv_state_out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+int gdn_prefill_packed_gate_logits(const gdn_shape *shape, const int32_t *cu_seqlens,
+                                   const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                   const float *a, const float *b, const float *A_log,
+                                   const float *dt_bias, const uint16_t *z, const uint16_t *conv_w,
+                                   const uint16_t *norm_w, const float *state_in,
+                                   const uint16_t *conv_state_in, uint16_t *o, float *state_out,
+                                   uint16_t *conv_state_out, void *workspace,
+                                   size_t workspace_bytes, void *stream);
 
 /* A static, NUL-terminated description of a status code. */
 const char *gdn_status_string(int status);

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["gdn_decode_step", "gdn_decode_step_gate_logits", "gdn_last_error", "gdn_prefill",
-         "gdn_prefill_gate_logits", "gdn_prefill_workspace_size", "gdn_state_init", "gdn_status_string"])
+         "gdn_prefill_gate_logits", "gdn_prefill_packed", "gdn_prefill_packed_gate_logits",
+         "gdn_prefill_workspace_size", "gdn_state_init", "gdn_status_string"])
 
 
 def test_last_error_is_a_string_before_any_failure():
@@ -181,6 +182,49 @@ def test_gate_logit_entry_points_reject_bad_arguments():
     bad = list(ok)
     bad[6] = ok[12]  # dt_bias inside o
     assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
+
+
+def _call_packed(shape, cu, **over):
+    a = _prefill_args(shape, **over)
+    return gdn._lib.gdn_prefill_packed(C.byref(shape), cu, a["q"], a["k"], a["v"], a["g"], a["beta"], a["z"],
+                                       a["conv_w"], a["norm_w"], a["state_in"], a["conv_state_in"], a["o"],
+                                       a["state_out"], a["conv_state_out"], a["workspace"], a["workspace_bytes"],
+                                       None)
+
+
+def test_packed_workspace_covers_every_packing():
+    """Slots for floor(T / 64) + B chunks: the most that B sequences of T tokens in all
+    can have (each sequence's last chunk may be partial)."""
+    even = gdn.gdn_prefill_workspace_size(_shape(B=1, T=6400))
+    packed = gdn.gdn_prefill_workspace_size(_shape(B=100, T=6400, packed=True))
+    assert packed > even
+    many = gdn.gdn_prefill_workspace_size(_shape(B=6400, T=6400, packed=True))  # one token each
+    assert many >= 6400 * 2 * (2 * 64 * 128 + 128 * 64) * 2
+
+
+def test_packed_entry_points_reject_bad_arguments():
+    s = _shape(B=3, T=300, packed=True)
+    cu = FAKE + (1 << 36)                       # the [B + 1] offsets, far from everything else
+    assert _call_packed(s, None) == gdn.GDN_EINVAL
+    assert _call_packed(s, cu + 2) == gdn.GDN_EINVAL               # 4-byte alignment
+    a = _prefill_args(s)
+    assert _call_packed(s, a["o"]) == gdn.GDN_EINVAL               # offsets inside o
+    assert _call_packed(s, a["workspace"]) == gdn.GDN_EINVAL       # offsets inside the workspace
+    assert _call_packed(s, cu, q=None) == gdn.GDN_EINVAL
+    assert _call_packed(s, cu, workspace_bytes=gdn.gdn_prefill_workspace_size(s) - 1) == gdn.GDN_EWORKSPACE
+    even = _shape(B=3, T=300)
+    assert _call_packed(even, cu) == gdn.GDN_EINVAL                # the shape must carry GDN_PACKED
+    assert _call_prefill(s, workspace_bytes=1 << 40) == gdn.GDN_EINVAL   # and gdn_prefill refuses it
+    f = gdn._lib.gdn_prefill_packed_gate_logits
+    a = _prefill_args(s)
+    gates = a["workspace"] + (1 << 34)
+    args = [a["q"], a["k"], a["v"], a["g"], a["beta"]]
+    rest = [a["z"], a["conv_w"], a["norm_w"], a["state_in"], a["conv_state_in"], a["o"], a["state_out"],
+            a["conv_state_out"], a["workspace"], a["workspace_bytes"], None]
+    assert f(C.byref(s), cu, *args, None, gates, *rest) == gdn.GDN_EINVAL
+    assert f(C.byref(s), None, *args, gates, gates + 1024, *rest) == gdn.GDN_EINVAL
+    ok = [FAKE + i * (64 * MB) for i in range(11)]
+    assert gdn._lib.gdn_decode_step(C.byref(s), *ok, None) == gdn.GDN_EINVAL  # decode has nothing to pack
 
 
 def test_state_init_rejects_bad_arguments():
