@@ -7,7 +7,8 @@ One step = one gdn_prefill call over the whole batch of the headline workload
 L2 norm, gated delta rule, gated RMSNorm), inputs already resident in HBM.
 Prints ONE JSON line.  `value` is prefill tokens/s of the layer.  Extra fields
 carry the roofline of the timed call, the decode step on the 27B-shaped
-B=256 workload (state GB/s, % of HBM), the other prefill shapes, and the fp64
+B=256 workload (state GB/s, % of HBM), the other prefill shapes, the 4B-shaped
+layer's tokens as 16 packed sequences of mixed lengths, and the fp64
 CPU oracle timed on this host (a reported baseline, not a target).
 
 Inputs are synthetic and seeded (torch's generator on the GPU for the timed
@@ -42,6 +43,18 @@ WORKLOADS = {
     "qwen38_27b_prefill_T262144": (1, 262144, 16, 48),
 }
 DECODE = ("qwen38_27b_decode_B256", (256, 16, 48))
+# packed sequences: the 4B-shaped layer's 65536 tokens as 16 sequences of mixed lengths
+PACKED = ("qwen35_4b_prefill_packed_16seq_T65536", (16, 65536, 16, 32))
+
+
+def packed_lengths(n, total, seed=3000):
+    """n seeded sequence lengths summing to total, spread over a 1:8 range of weights."""
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([20261202, seed])))
+    w = rng.uniform(0.25, 2.0, size=n)
+    lens = np.maximum(1, np.floor(w / w.sum() * total)).astype(np.int64)
+    lens[-1] += total - lens.sum()
+    return lens.tolist()
 
 
 def prefill_bytes(B, T, Hk, Hv) -> int:
@@ -157,6 +170,41 @@ def bench_prefill(torch, gdn, name, steps, warmup, gate_logits=False):
         "input_sets": nsets, "steps": steps, "wall_s": wall,
     }
     del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill_packed(torch, gdn, steps, warmup):
+    """One gdn_prefill_packed call over the 4B-shaped layer's tokens, split into
+    sequences of mixed lengths (each restarts its state and conv window)."""
+    name, (N, T, Hk, Hv) = PACKED
+    lens = packed_lengths(N, T)
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32, device="cuda")
+    Cc = 2 * Hk * D + Hv * D
+    d = make_prefill_set(torch, gdn, 1, T, Hk, Hv, seed=1100)
+    d["state_out"] = torch.empty((N, Hv, D, D), dtype=torch.float32, device="cuda")
+    d["conv_state_out"] = torch.empty((N, 3, Cc), dtype=torch.bfloat16, device="cuda")
+    d["shape"] = gdn.make_shape(N, T, Hk, Hv, packed=True)
+    d["ws"] = torch.zeros(gdn.gdn_prefill_workspace_size(d["shape"]), dtype=torch.uint8, device="cuda")
+    d["cu"] = cu
+    torch.cuda.synchronize()
+
+    def run(dd):
+        gdn.gdn_prefill_packed(dd["shape"], dd["cu"], dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["z"],
+                               dd["conv_w"], dd["norm_w"], None, None, dd["o"], dd["state_out"],
+                               dd["conv_state_out"], dd["ws"])
+    ms, wall = time_calls(torch, run, [d], steps, warmup)
+    # per-token bytes as the even batch; one final state and conv tail per sequence
+    nbytes = prefill_bytes(1, T, Hk, Hv) + (N - 1) * (Hv * D * D * 4 + 3 * Cc * 2)
+    flops = USEFUL_FLOP_PER_TOKEN_HEAD * T * Hv
+    res = {
+        "workload": name + " (gdn_prefill_packed)", "sequences": N, "T_total": T, "Hk": Hk, "Hv": Hv,
+        "lengths_min_max": [min(lens), max(lens)], "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+        "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": nbytes / (ms * 1e-3) / HBM_PEAK, "useful_TFLOPs": flops / (ms * 1e-3) / 1e12,
+        "mfma_useful_frac": flops / (ms * 1e-3) / MFMA_FP16_PEAK, "steps": steps, "wall_s": wall,
+    }
+    del d
     torch.cuda.empty_cache()
     return res
 
@@ -296,6 +344,8 @@ def main(argv=None):
                 B, T, Hk, Hv = WORKLOADS[name]
                 steps = max(3, min(args.steps, int(2e8 // (B * T * Hv))))
                 extra[name] = bench_prefill(torch, gdn, name, steps, 2)
+        # the 4B-shaped layer's tokens as packed sequences of mixed lengths
+        extra[PACKED[0]] = bench_prefill_packed(torch, gdn, 20, 2)
         # the same layer through the entry point that takes the gate logits
         extra[args.workload + "_gate_logits"] = bench_prefill(torch, gdn, args.workload, max(20, args.steps // 4), 5,
                                                               gate_logits=True)

@@ -117,7 +117,12 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
  *                 completes leaves its exchange area zeroed again and its
  *                 readiness words holding a per-call stamp that no later call
  *                 in the process reuses (stamps wrap after 2^31 calls).  Calls
- *                 that run concurrently must not share a workspace.
+ *                 that run concurrently must not share a workspace.  The one
+ *                 exception to the clean exchange area is the error word, the
+ *                 first 32-bit word of the workspace's last 256 bytes: bit 0 says
+ *                 a bounded cross-workgroup wait timed out (the outputs are then
+ *                 wrong), bit 1 that gdn_prefill_packed skipped a sequence with
+ *                 invalid bounds.  It keeps its bits until the caller clears it.
  *
  * `o` must not overlap any input.  Returns GDN_OK once the work is enqueued.
  */
