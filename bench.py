@@ -7,7 +7,8 @@ One step = one gdn_prefill call over the whole batch of the headline workload
 L2 norm, gated delta rule, gated RMSNorm), inputs already resident in HBM.
 Prints ONE JSON line.  `value` is prefill tokens/s of the layer.  Extra fields
 carry the roofline of the timed call, the decode step on the 27B-shaped
-B=256 workload (state GB/s, % of HBM), the other prefill shapes, the 4B-shaped
+B=256 workload (state GB/s, % of HBM) and the same batch checking two tokens per
+sequence with snapshots, the other prefill shapes, the 4B-shaped
 layer's tokens as 16 packed sequences of mixed lengths, and the fp64
 CPU oracle timed on this host (a reported baseline, not a target).
 
@@ -241,6 +242,51 @@ def bench_decode(torch, gdn, steps, warmup):
     return res
 
 
+def decode_multi_bytes(B, T, Hk, Hv) -> int:
+    """Algorithmic HBM bytes of one T-token decode call with snapshots: the state read once and
+    written T times (T - 1 snapshots and the final state), the conv window read once and written
+    T times, T tokens of q,k,v,z,g,beta in and of o out, weights."""
+    Cc = 2 * Hk * D + Hv * D
+    return ((1 + T) * B * Hv * D * D * 4 + (1 + T) * B * 3 * Cc * 2
+            + T * (B * Hk * D * 2 * 2 + B * Hv * D * 2 * 3 + B * Hv * 8) + Cc * 4 * 2 + D * 2)
+
+
+def bench_decode_multi(torch, gdn, steps, warmup, T=2):
+    """The 27B-shaped decode batch checking T tokens per sequence in one gdn_decode_multi call,
+    with state and conv snapshots after every token but the last."""
+    B, Hk, Hv = DECODE[1]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(78)
+    Cc = 2 * Hk * D + Hv * D
+    d = dict(
+        q=_gen(torch, gen, (B, T, Hk, D), "normal_bf16"), k=_gen(torch, gen, (B, T, Hk, D), "normal_bf16"),
+        v=_gen(torch, gen, (B, T, Hv, D), "normal_bf16"), z=_gen(torch, gen, (B, T, Hv, D), "normal_bf16"),
+        g=_gen(torch, gen, (B, T, Hv), "g"), beta=_gen(torch, gen, (B, T, Hv), "beta"),
+        conv_w=(torch.randn((Cc, 4), generator=gen, device="cuda") * 0.5).to(torch.bfloat16),
+        norm_w=(1.0 + 0.02 * torch.randn((D,), generator=gen, device="cuda")).to(torch.bfloat16),
+        state=torch.randn((B, Hv, D, D), generator=gen, device="cuda") * 0.1,
+        conv_state=_gen(torch, gen, (B, 3, Cc), "normal_bf16"),
+        o=torch.empty((B, T, Hv, D), dtype=torch.bfloat16, device="cuda"),
+        state_snaps=torch.empty((T - 1, B, Hv, D, D), device="cuda"),
+        conv_snaps=torch.empty((T - 1, B, 3, Cc), dtype=torch.bfloat16, device="cuda"),
+    )
+    shape = gdn.make_shape(B, T, Hk, Hv)
+
+    def fn(dd):
+        gdn.gdn_decode_multi(shape, dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["z"], dd["conv_w"],
+                             dd["norm_w"], dd["state"], dd["conv_state"], dd["o"], dd["state_snaps"],
+                             dd["conv_snaps"])
+    ms, wall = time_calls(torch, fn, [d], steps, warmup)
+    nbytes = decode_multi_bytes(B, T, Hk, Hv)
+    res = {"workload": f"{DECODE[0]} checking T={T} tokens per sequence (gdn_decode_multi, snapshots)",
+           "B": B, "T": T, "Hk": Hk, "Hv": Hv, "us_per_call": ms * 1e3, "tokens_per_s": B * T / (ms * 1e-3),
+           "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
+           "hbm_frac": nbytes / (ms * 1e-3) / HBM_PEAK, "steps": steps}
+    del d
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, budget_s=20.0, min_s=10.0):
     """The fp64 oracle (as it stands) on this host's cores, on the headline
     workload: all of its (sequence, value-head) chains, repeated until about
@@ -339,6 +385,7 @@ def main(argv=None):
     extra = {}
     if not args.no_extra:
         extra["decode"] = bench_decode(torch, gdn, max(20, args.steps // 4), 5)
+        extra["decode_multi_T2"] = bench_decode_multi(torch, gdn, max(20, args.steps // 4), 5)
         for name in WORKLOADS:
             if name != args.workload:
                 B, T, Hk, Hv = WORKLOADS[name]

@@ -71,11 +71,14 @@ _lib.gdn_decode_step.argtypes = [_sp] + [_vp] * 12
 _lib.gdn_prefill_gate_logits.argtypes = [_sp] + [_vp] * 16 + [C.c_size_t, _vp]
 _lib.gdn_decode_step_gate_logits.argtypes = [_sp] + [_vp] * 14
 _lib.gdn_prefill_packed.argtypes = [_sp] + [_vp] * 15 + [C.c_size_t, _vp]
+_lib.gdn_decode_multi.argtypes = [_sp] + [_vp] * 14
+_lib.gdn_decode_multi_gate_logits.argtypes = [_sp] + [_vp] * 16
 _lib.gdn_prefill_packed_gate_logits.argtypes = [_sp] + [_vp] * 17 + [C.c_size_t, _vp]
 
 EXPORTED = ("gdn_state_init", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
             "gdn_prefill_gate_logits", "gdn_decode_step_gate_logits", "gdn_prefill_packed",
-            "gdn_prefill_packed_gate_logits", "gdn_status_string", "gdn_last_error")
+            "gdn_prefill_packed_gate_logits", "gdn_decode_multi", "gdn_decode_multi_gate_logits",
+            "gdn_status_string", "gdn_last_error")
 
 
 def _ptr(t):
@@ -179,3 +182,21 @@ def gdn_prefill_packed_gate_logits(shape: gdn_shape, cu_seqlens, q, k, v, a, b, 
         _ptr(dt_bias), _ptr(z), _ptr(conv_w), _ptr(norm_w), _ptr(state_in), _ptr(conv_state_in), _ptr(o),
         _ptr(state_out), _ptr(conv_state_out), _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check("gdn_prefill_packed_gate_logits", rc)
+
+
+def gdn_decode_multi(shape: gdn_shape, q, k, v, g, beta, z, conv_w, norm_w, state, conv_state, o,
+                     state_snaps=None, conv_snaps=None, stream=None) -> None:
+    """shape.T tokens per sequence (1..8); state and conv_state are updated in place."""
+    rc = _lib.gdn_decode_multi(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
+                               _ptr(conv_w), _ptr(norm_w), _ptr(state), _ptr(conv_state), _ptr(o),
+                               _ptr(state_snaps), _ptr(conv_snaps), _stream(stream))
+    _check("gdn_decode_multi", rc)
+
+
+def gdn_decode_multi_gate_logits(shape: gdn_shape, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state,
+                                 conv_state, o, state_snaps=None, conv_snaps=None, stream=None) -> None:
+    rc = _lib.gdn_decode_multi_gate_logits(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b),
+                                           _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(conv_w), _ptr(norm_w),
+                                           _ptr(state), _ptr(conv_state), _ptr(o), _ptr(state_snaps),
+                                           _ptr(conv_snaps), _stream(stream))
+    _check("gdn_decode_multi_gate_logits", rc)

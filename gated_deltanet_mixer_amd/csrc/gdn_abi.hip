@@ -152,12 +152,15 @@ int prefill_impl(const gdn_shape *s, const int32_t *cu_seqlens, const uint16_t *
     return launch_prefill(p, plan, static_cast<hipStream_t>(stream)) ? GDN_EHIP : GDN_OK;
 }
 
-int decode_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+// T tokens per sequence (1 for gdn_decode_step); the snapshots are used only when T > 1.
+int decode_impl(const gdn_shape *s, int T, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                 const float *beta, const float *A_log, const float *dt_bias, const uint16_t *z,
                 const uint16_t *conv_w, const uint16_t *norm_w, float *state, uint16_t *conv_state, uint16_t *o,
-                void *stream) {
+                float *state_snaps, uint16_t *conv_snaps, void *stream) {
     int rc = check_shape(s, false);
     if (rc) return rc;
+    if (T < 1 || T > kMaxDecodeTokens) return GDN_EINVAL;
+    if (T == 1) state_snaps = nullptr, conv_snaps = nullptr;
     if (s->flags & GDN_PACKED) return GDN_EINVAL;  // one token per sequence: nothing to pack
     if ((A_log == nullptr) != (dt_bias == nullptr)) return GDN_EINVAL;
     if (A_log && (!aligned(A_log, 4) || !aligned(dt_bias, 4))) return GDN_EINVAL;
@@ -166,32 +169,40 @@ int decode_impl(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const 
     if (!q || !k || !v || !g || !beta || !o || !state) return GDN_EINVAL;
     if (norm && (!z || !norm_w)) return GDN_EINVAL;
     if (conv != (conv_w != nullptr) || conv != (conv_state != nullptr)) return GDN_EINVAL;
-    const void *a16[] = {q, k, v, z, conv_w, norm_w, state, conv_state, o};
+    if (!conv && conv_snaps) return GDN_EINVAL;
+    const void *a16[] = {q, k, v, z, conv_w, norm_w, state, conv_state, o, state_snaps, conv_snaps};
     for (const void *p : a16)
         if (p && !aligned(p, 16)) return GDN_EINVAL;
     if (!aligned(g, 4) || !aligned(beta, 4)) return GDN_EINVAL;
     if (s->Hv / s->Hk > 64) return GDN_EUNSUPPORTED;  // the r value heads' conv outputs must fit one workgroup's LDS
+    if (decode_lds_bytes(T, s->Hv / s->Hk) > 160 * 1024) return GDN_EUNSUPPORTED;
 
     const size_t B = s->B, Hk = s->Hk, Hv = s->Hv, Cc = conv_channels(s);
-    const size_t nqk = B * Hk * kD * 2, nv = B * Hv * kD * 2, ngb = B * Hv * 4;
+    const size_t nqk = B * T * Hk * kD * 2, nv = B * T * Hv * kD * 2, ngb = B * T * Hv * 4;
     const size_t nst = B * Hv * kD * kD * 4, ncs = B * 3 * Cc * 2;
     const size_t nw = conv ? Cc * 4 * 2 : 0, nn = norm ? kD * 2 : 0;
+    const size_t nss = (T - 1) * nst, ncss = (T - 1) * ncs;
     const struct {
         const void *p;
         size_t n;
     } ro[] = {{q, nqk}, {k, nqk}, {v, nv}, {g, ngb}, {beta, ngb}, {norm ? z : nullptr, nv},
               {conv_w, nw}, {norm_w, nn}, {A_log, Hv * 4}, {dt_bias, Hv * 4}};
-    for (const auto &in : ro)
-        if (overlap(o, nv, in.p, in.n) || overlap(state, nst, in.p, in.n) || overlap(conv_state, ncs, in.p, in.n))
-            return GDN_EINVAL;
-    if (overlap(o, nv, state, nst) || overlap(o, nv, conv_state, ncs) || overlap(state, nst, conv_state, ncs))
-        return GDN_EINVAL;
+    const struct {
+        const void *p;
+        size_t n;
+    } rw[] = {{o, nv}, {state, nst}, {conv_state, ncs}, {state_snaps, nss}, {conv_snaps, ncss}};
+    for (const auto &out : rw)
+        for (const auto &in : ro)
+            if (overlap(out.p, out.n, in.p, in.n)) return GDN_EINVAL;
+    for (size_t i = 0; i < 5; ++i)
+        for (size_t j = i + 1; j < 5; ++j)
+            if (overlap(rw[i].p, rw[i].n, rw[j].p, rw[j].n)) return GDN_EINVAL;
 
     DecodeParams p;
     p.q = q; p.k = k; p.v = v; p.z = norm ? z : nullptr; p.conv_w = conv_w; p.norm_w = norm ? norm_w : nullptr;
     p.g = g; p.beta = beta; p.A_log = A_log; p.dt_bias = dt_bias;
-    p.state = state; p.conv_state = conv_state; p.o = o;
-    p.B = s->B; p.Hk = s->Hk; p.Hv = s->Hv; p.conv_width = s->conv_width; p.norm = norm;
+    p.state = state; p.conv_state = conv_state; p.o = o; p.state_snaps = state_snaps; p.conv_snaps = conv_snaps;
+    p.B = s->B; p.T = T; p.Hk = s->Hk; p.Hv = s->Hv; p.conv_width = s->conv_width; p.norm = norm;
     p.eps_l2 = s->eps_l2; p.eps_norm = s->eps_norm;
     return launch_decode(p, static_cast<hipStream_t>(stream)) ? GDN_EHIP : GDN_OK;
 }
@@ -243,7 +254,8 @@ int gdn_prefill_packed_gate_logits(const gdn_shape *s, const int32_t *cu_seqlens
 int gdn_decode_step(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                     const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
                     float *state, uint16_t *conv_state, uint16_t *o, void *stream) {
-    return decode_impl(s, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state, conv_state, o, stream);
+    return decode_impl(s, 1, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state, conv_state, o, nullptr,
+                       nullptr, stream);
 }
 
 int gdn_decode_step_gate_logits(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -251,7 +263,27 @@ int gdn_decode_step_gate_logits(const gdn_shape *s, const uint16_t *q, const uin
                                 const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w, float *state,
                                 uint16_t *conv_state, uint16_t *o, void *stream) {
     if (!A_log || !dt_bias) return GDN_EINVAL;
-    return decode_impl(s, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state, conv_state, o, stream);
+    return decode_impl(s, 1, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state, conv_state, o, nullptr, nullptr,
+                       stream);
+}
+
+int gdn_decode_multi(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                     const float *beta, const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w,
+                     float *state, uint16_t *conv_state, uint16_t *o, float *state_snaps, uint16_t *conv_snaps,
+                     void *stream) {
+    if (!s) return GDN_EINVAL;
+    return decode_impl(s, s->T, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state, conv_state, o,
+                       state_snaps, conv_snaps, stream);
+}
+
+int gdn_decode_multi_gate_logits(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const float *a, const float *b, const float *A_log, const float *dt_bias,
+                                 const uint16_t *z, const uint16_t *conv_w, const uint16_t *norm_w, float *state,
+                                 uint16_t *conv_state, uint16_t *o, float *state_snaps, uint16_t *conv_snaps,
+                                 void *stream) {
+    if (!s || !A_log || !dt_bias) return GDN_EINVAL;
+    return decode_impl(s, s->T, q, k, v, a, b, A_log, dt_bias, z, conv_w, norm_w, state, conv_state, o, state_snaps,
+                       conv_snaps, stream);
 }
 
 } // extern "C"

@@ -7,12 +7,16 @@
 namespace gdn {
 
 // g and beta hold the gate logits a and b when A_log and dt_bias are set.
+constexpr int kMaxDecodeTokens = 8;  // tokens per sequence of one decode call
+
 struct DecodeParams {
     const uint16_t *q, *k, *v, *z, *conv_w, *norm_w;
     const float *g, *beta, *A_log, *dt_bias;
     float *state;
     uint16_t *conv_state, *o;
-    int B, Hk, Hv, conv_width, norm;
+    float *state_snaps;    // [T-1][B][Hv][128][128] or nullptr
+    uint16_t *conv_snaps;  // [T-1][B][3][Cc] or nullptr
+    int B, T, Hk, Hv, conv_width, norm;  // T: tokens per sequence, 1..8
     float eps_l2, eps_norm;
 };
 
@@ -48,6 +52,7 @@ int fail(const char *what);
 
 int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan);
 int launch_decode(const DecodeParams &p, hipStream_t stream);
+size_t decode_lds_bytes(int T, int r);  // LDS of one decode workgroup
 int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream);
 int launch_state_init(float *state, size_t n_state, uint16_t *conv_state, size_t n_conv,
                       hipStream_t stream);

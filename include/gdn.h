@@ -61,7 +61,7 @@ extern "C" {
 
 typedef struct gdn_shape {
     int32_t B;          /* sequences, >= 1 */
-    int32_t T;          /* tokens per sequence, >= 1 (gdn_decode_step ignores it) */
+    int32_t T;          /* tokens per sequence, >= 1 (gdn_decode_step ignores it; gdn_decode_multi: 1..8) */
     int32_t Hk;         /* key / query heads, >= 1 */
     int32_t Hv;         /* value heads, a multiple of Hk */
     int32_t Dk;         /* key head width: must be 128 */
@@ -178,6 +178,48 @@ int gdn_decode_step_gate_logits(const gdn_shape *shape, const uint16_t *q, const
                                 const float *A_log, const float *dt_bias, const uint16_t *z,
                                 const uint16_t *conv_w, const uint16_t *norm_w, float *state,
                                 uint16_t *conv_state, uint16_t *o, void *stream);
+
+/*
+ * T decode steps in one call: T new tokens per sequence (1 <= T <= 8), for
+ * checking draft tokens in one pass ("Qwen3.5-4B architecture", multi-token
+ * prediction: a draft head proposes tokens and one forward pass verifies
+ * them).  The tokens run through the recurrence one after the other exactly
+ * as T calls of gdn_decode_step would; the state is read once and stays on
+ * chip between the tokens.  A recurrent state cannot be rewound, so rolling
+ * back to an accepted prefix needs snapshots ("How Qwen3.5 works" §13.5):
+ * when state_snaps / conv_snaps are given, the state and the conv window
+ * after each token t < T-1 are written there; after the last token they go
+ * to state / conv_state in place.  Accepting tokens 0..j (j < T-1) then means
+ * continuing from snapshot j.
+ *
+ *  shape->T    tokens per sequence, 1..8
+ *  q, k        [B][T][Hk][128] bf16;  v, z, o  [B][T][Hv][128] bf16
+ *  g, beta     [B][T][Hv] fp32 (gdn_decode_multi_gate_logits: the logits a, b,
+ *              with A_log and dt_bias [Hv] as in gdn_prefill_gate_logits)
+ *  state       [B][Hv][128][128] fp32, read, then overwritten with the state
+ *              after the last token
+ *  conv_state  [B][3][Cc] bf16, read, then overwritten with the window after
+ *              the last token (NULL iff conv_width == 0)
+ *  state_snaps [T-1][B][Hv][128][128] fp32 or NULL: snapshot t (one state
+ *              tensor of the same layout as state) after token t
+ *  conv_snaps  [T-1][B][3][Cc] bf16 or NULL (must be NULL when conv_width == 0)
+ *
+ * With T = 1 the snapshots are not used and the call is gdn_decode_step.  The
+ * snapshots are outputs: they must not overlap any other argument.  Returns
+ * GDN_EINVAL for T outside 1..8 and GDN_EUNSUPPORTED when T and Hv/Hk need
+ * more on-chip memory than one workgroup has; otherwise as gdn_decode_step.
+ */
+int gdn_decode_multi(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
+                     const uint16_t *v, const float *g, const float *beta, const uint16_t *z,
+                     const uint16_t *conv_w, const uint16_t *norm_w, float *state,
+                     uint16_t *conv_state, uint16_t *o, float *state_snaps, uint16_t *conv_snaps,
+                     void *stream);
+int gdn_decode_multi_gate_logits(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
+                                 const uint16_t *v, const float *a, const float *b,
+                                 const float *A_log, const float *dt_bias, const uint16_t *z,
+                                 const uint16_t *conv_w, const uint16_t *norm_w, float *state,
+                                 uint16_t *conv_state, uint16_t *o, float *state_snaps,
+                                 uint16_t *conv_snaps, void *stream);
 
 /*
  * Prefill over packed sequences of different lengths, one call for the whole

@@ -26,6 +26,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["gdn_decode_step", "gdn_decode_step_gate_logits", "gdn_last_error", "gdn_prefill",
          "gdn_prefill_gate_logits", "gdn_prefill_packed", "gdn_prefill_packed_gate_logits",
+         "gdn_decode_multi", "gdn_decode_multi_gate_logits",
          "gdn_prefill_workspace_size", "gdn_state_init", "gdn_status_string"])
 
 
@@ -225,6 +226,35 @@ def test_packed_entry_points_reject_bad_arguments():
     assert f(C.byref(s), None, *args, gates, gates + 1024, *rest) == gdn.GDN_EINVAL
     ok = [FAKE + i * (64 * MB) for i in range(11)]
     assert gdn._lib.gdn_decode_step(C.byref(s), *ok, None) == gdn.GDN_EINVAL  # decode has nothing to pack
+
+
+def test_decode_multi_rejects_bad_arguments():
+    # q, k, v, g, beta, z, conv_w, norm_w, state, conv_state, o, state_snaps, conv_snaps
+    ok = [FAKE + i * (256 * MB) for i in range(13)]
+    f = gdn._lib.gdn_decode_multi
+    for T, code in ((0, gdn.GDN_EINVAL), (9, gdn.GDN_EINVAL)):
+        assert f(C.byref(_shape(T=T)), *ok, None) == code, T
+    s = _shape(T=4)
+    bad = list(ok)
+    bad[11] = ok[8] + 65536             # snapshots inside the state
+    assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
+    bad = list(ok)
+    bad[12] = ok[0]                     # conv snapshots on top of q
+    assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
+    bad = list(ok)
+    bad[11] = ok[11] + 8                # 16-byte alignment
+    assert f(C.byref(s), *bad, None) == gdn.GDN_EINVAL
+    s0 = _shape(T=4, conv=False)        # conv snapshots without a conv
+    bad = list(ok)
+    bad[6] = bad[9] = None
+    assert f(C.byref(s0), *bad, None) == gdn.GDN_EINVAL
+    bad[12] = None
+    assert f(C.byref(_shape(T=8, Hk=1, Hv=64)), *ok, None) == gdn.GDN_EUNSUPPORTED  # LDS of 8 tokens x 64 heads
+    g = gdn._lib.gdn_decode_multi_gate_logits
+    okg = ok[:5] + [FAKE + 13 * 256 * MB, FAKE + 14 * 256 * MB] + ok[5:]
+    bad = list(okg)
+    bad[5] = None                       # A_log missing
+    assert g(C.byref(s), *bad, None) == gdn.GDN_EINVAL
 
 
 def test_state_init_rejects_bad_arguments():
