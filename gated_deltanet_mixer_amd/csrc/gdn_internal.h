@@ -42,6 +42,9 @@ struct PrefillPlan {
     size_t tp_bytes;     // per (slot, value head): T diag(beta), P (lower blocks, fp16), decay vectors
     size_t ready_bytes;  // per (slot, key head): stamp of the call whose operands are written
     size_t mbox_bytes;   // exchange area (tagged partial sums, counters, error word)
+    int nseg;            // segments per sequence of the two-level scan (1: the plain sequential pass)
+    int seg_chunks;      // chunks per segment
+    size_t seg_out_bytes, seg_state_bytes, seg_frag_bytes;  // two-level scan: read-outs, segment maps, start states
     size_t total_bytes;
 };
 

@@ -51,6 +51,7 @@
 //                     is bounded.
 // All contractions use fp16 MFMA operands with fp32 accumulation; the state is
 // carried in fp32 across chunks; inputs and outputs are bf16.
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <mutex>
@@ -621,6 +622,10 @@ struct ChainArgs {
     const unsigned int *ready; // [slots][Hk] prep stamps
     unsigned int stamp;
     const int *cu;             // packed sequences: [B + 1] token offsets (nullptr: even batch)
+    // segment pass (two-level scan): segments of seg_chunks chunks, nseg per sequence
+    _Float16 *seg_out;         // per (chunk slot, value head) kSegBlk halves: R as MFMA A fragments, O0 rows
+    float *seg_state;          // [B Hv nseg][128][256] fp32: final [M | N] of each segment
+    int nseg, seg_chunks;
     int B, T, Hk, Hv, r, Cc, conv, norm, nch, n_items, grid;
     float eps_norm;
 };
@@ -826,6 +831,13 @@ __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, u
 
 __device__ __forceinline__ int mod3(int x) { return ((x % 3) + 3) % 3; }
 
+// Two-level scan: what the first pass hands the last one per (chunk slot, value head), in fp16:
+// R [64][128] (the read-out of the transition columns) as 16 MFMA A-operand fragments
+// (row tile rt, k-step ks: lane l16 + 16 lq holds row 16 rt + l16 at columns 32 ks + 4 lq + e
+// and 32 ks + 16 + 4 lq + e), then O0 [64][128] (the zero-start read-out) row-major.
+constexpr int kSegR = 16 * kFrag;
+constexpr int kSegBlk = kSegR + kC * kD;
+
 
 // The prep kernel may still be running while this one starts: prep block
 // (operand slot gc, key head kh) stores this call's stamp once its operands
@@ -853,11 +865,19 @@ __device__ __forceinline__ void wait_ready(const ChainArgs &a, int gc, int kh, i
     }
 }
 
-template <int NT>
+// SEG = false: the sequential pass over whole sequences (state_in -> outputs, state_out).
+// SEG = true: the first pass of the two-level scan.  Every segment of seg_chunks chunks
+// runs on its own, with 256 virtual value columns per head: columns 0..127 start from
+// the identity and carry no values (their state ends as the segment's transition M,
+// their read-out as R, so that O = R S_start is what the start state adds to the
+// outputs), columns 128..255 start from zero with the real values (state N, read-out
+// O0).  A segment's outputs are then O0 + R S_start and its final state M S_start + N
+// (the segment map is affine in the start state), which the two later kernels apply.
+template <int NT, bool SEG>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void chain_kernel(ChainArgs a) {
     using L = ChainLds<NT>;
     constexpr int BV = L::BV, VT = L::VT;
-    constexpr int NSL = kTiles / NT;
+    constexpr int NSL = (SEG ? 2 : 1) * kTiles / NT;
     constexpr int NCG = BV / 8;                 // 8-column groups per slice row
     constexpr int NV = 8 - 2 * NT - 1;          // VALU helper waves
     // Helper 0 runs the norm's exchange; helpers 1 and 2 gate; conv(v) runs on the rest
@@ -901,7 +921,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // running or next in line for the next free workgroup, and no launch-wide
     // co-residency is needed.
     const int xcc = static_cast<int>(xcc_id() & 7u);
-    const int n_chains = a.B * a.Hv;
+    const int n_chains = a.B * a.Hv * (SEG ? a.nseg : 1);  // (head, segment) pairs in the segment pass
+    const bool norm = !SEG && a.norm;                       // the segment pass leaves the norm to the last kernel
     int qi = 0;
 
     for (;;) {
@@ -932,11 +953,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int item = __builtin_amdgcn_readfirstlane(s_item);  // uniform: addresses stay scalar
         __syncthreads();
         if (item < 0) break;
-        const int chain = item / NSL, s = item % NSL;
+        const int vchain = item / NSL, s = item % NSL;
+        const int chain = SEG ? vchain / a.nseg : vchain, seg = SEG ? vchain % a.nseg : 0;
         const int b = chain / a.Hv, h = chain % a.Hv, kh = h / a.r;
-        const SeqInfo si = seq_info(a.cu, b, a.T, a.nch);
-        const int nch = si.nch, sc0 = si.c0;
-        const int sv0 = s * BV;
+        const SeqInfo si = seq_info(a.cu, b, a.T, a.nch);  // the whole sequence
+        SeqInfo ss = si;                                    // the stretch this item runs over
+        if (SEG) {
+            const int cb = seg * a.seg_chunks;
+            ss.tok0 = si.tok0 + (size_t)cb * kC;
+            ss.T = min(si.T - cb * kC, a.seg_chunks * kC);
+            ss.c0 = si.c0 + cb;
+            ss.nch = min(si.nch - cb, a.seg_chunks);
+        }
+        const int nch = ss.nch, sc0 = ss.c0;
+        const int vcol0 = s * BV;                 // virtual column (0..255 in the segment pass)
+        const bool mcol = SEG && vcol0 < kD;      // transition columns: identity start, no values
+        const int sv0 = vcol0 % kD;               // value column of the slice
         const int last = nch + 2 + kLag;
         const size_t qk_stride = (size_t)a.Hk * kQKF, tp_stride = (size_t)a.Hv * kTPF;
         const _Float16 *qk0 = a.qkf + ((size_t)sc0 * a.Hk + kh) * kQKF;
@@ -956,7 +988,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             wait_ready(a, sc0, kh, broken);
             state_load(fr, tp0, lane, lq);
             floatx4 S[8];
-            {
+            if (SEG) {
+#pragma unroll
+                for (int ti = 0; ti < 8; ++ti)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S[ti][e] = (mcol && 16 * ti + 4 * lq + e == sv0 + jc) ? 1.0f : 0.0f;
+            } else {
                 const float *src = a.state_in ? a.state_in + (size_t)chain * kD * kD : nullptr;
 #pragma unroll
                 for (int ti = 0; ti < 8; ++ti)
@@ -971,11 +1008,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     state_step<NT>(smem, S, fr, tp0 + min(c + 1, nch - 1) * tp_stride, c, wave, lane, jc, lq, trofs);
                 lds_barrier();
             }
+            if (SEG) {
 #pragma unroll
-            for (int ti = 0; ti < 8; ++ti)
+                for (int ti = 0; ti < 8; ++ti)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    a.state_out[(size_t)chain * kD * kD + (size_t)(16 * ti + 4 * lq + e) * kD + sv0 + jc] = S[ti][e];
+                    for (int e = 0; e < 4; ++e)
+                        a.seg_state[((size_t)vchain * kD + 16 * ti + 4 * lq + e) * (2 * kD) + vcol0 + jc] = S[ti][e];
+            } else {
+#pragma unroll
+                for (int ti = 0; ti < 8; ++ti)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        a.state_out[(size_t)chain * kD * kD + (size_t)(16 * ti + 4 * lq + e) * kD + sv0 + jc] = S[ti][e];
+            }
         } else if (is_b) {
             // ---------------------------------------------------------- output wave
             const int t = wave - NT, jc = 16 * t + l16;
@@ -997,9 +1042,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // lane -> row (64 / NRD rows per instruction), 8-column group
             auto rows_dma = [&](const uint16_t *x, int cc, uint16_t *dst) __attribute__((always_inline)) {
                 const int c0 = min(max(cc, 0), nch - 1) * kC;
-                const unsigned int nrow = (unsigned int)min(si.T - c0, kC);
+                const unsigned int nrow = (unsigned int)min(ss.T - c0, kC);
                 const __amdgpu_buffer_rsrc_t r =
-                    make_rsrc(x + (si.tok0 + c0) * a.Hv * kD, nrow * (unsigned int)a.Hv * kD * 2);
+                    make_rsrc(x + (ss.tok0 + c0) * a.Hv * kD, nrow * (unsigned int)a.Hv * kD * 2);
 #pragma unroll
                 for (int u = 0; u < NRD; ++u) {
                     const int i = lane + 64 * u, row = i / NCG, cg = i % NCG;
@@ -1013,7 +1058,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int f = 0; f < 16; ++f) dma16(kb + f * kFrag + kswz(lane) * 8, slot + f * 1024);
             };
-            const uint16_t *zsrc = a.norm ? a.z : a.v;
+            const uint16_t *zsrc = norm ? a.z : a.v;
             // prologue: operands of chunks 0 and 1, raw v of chunks 0..2.  The load wave is
             // the one that waits for the prep blocks: A and B load a chunk's operands only
             // after the barrier that follows its wait.
@@ -1075,15 +1120,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4)
                     sCW[vtid * 4 + t4] = a.conv ? bf16_to_f32(a.conv_w[(size_t)chn * 4 + t4]) : 0.0f;
-                sNW[vtid] = a.norm ? bf16_to_f32(a.norm_w[sv0 + vtid]) : 1.0f;
+                sNW[vtid] = norm ? bf16_to_f32(a.norm_w[sv0 + vtid]) : 1.0f;
             }
             // conv-state rows (or zeros): the three raw rows before chunk 0
             if (vtid >= 64 && vtid < 64 + 3 * NCG) {
                 const int r3 = (vtid - 64) / NCG, cg = (vtid - 64) % NCG;
                 uint4 rw = make_uint4(0, 0, 0, 0);
-                if (a.conv && a.conv_state_in)
+                if (SEG && seg > 0) {  // a later segment: the raw rows before it are the sequence's own
+                    if (a.conv && !mcol)
+                        rw = *reinterpret_cast<const uint4 *>(a.v + ((ss.tok0 - 3 + r3) * a.Hv + h) * kD + sv0 + cg * 8);
+                } else if (a.conv && a.conv_state_in && !mcol) {
                     rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + r3) * a.Cc + 2 * a.Hk * kD +
                                                           h * kD + sv0 + cg * 8);
+                }
                 *reinterpret_cast<uint4 *>(sHalo + r3 * BV + cg * 8) = rw;
             }
             // A lane always serves the same 8-column group (every helper role's lane count is a
@@ -1117,7 +1166,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int j = 0; j < 4; ++j) unpack_bf16x8(rw[j], x[j]);
                     float u8[8];
-                    if (a.conv) {
+                    if (mcol) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) u8[e] = 0.0f;
+                    } else if (a.conv) {
                         float acc[8], t8[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
@@ -1152,7 +1204,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     const uint4 zr = *reinterpret_cast<const uint4 *>(zt + row * BV);
                     const float rstd = rs[row];
                     __builtin_amdgcn_sched_barrier(0);
-                    if (a.norm) {
+                    if (SEG) {  // the raw read-out, for the last kernel (every row: rows past T are finite)
+                        _Float16 *blk = a.seg_out + ((size_t)(sc0 + oc) * a.Hv + h) * kSegBlk;
+                        const int col = sv0 + cgl * 8;
+                        if (mcol) {  // R: two 4-column pieces of one row, in two lanes of a fragment
+                            const int cc = col & 31, L0 = (row & 15) + 16 * ((cc & 15) >> 2);
+                            _Float16 *f = blk + (((row >> 4) * 4 + (col >> 5)) * 64 + L0) * 8 + 4 * (cc >> 4);
+                            *reinterpret_cast<half4 *>(f) = half4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2],
+                                                                  (_Float16)y[3]};
+                            *reinterpret_cast<half4 *>(f + 16 * 8) = half4{(_Float16)y[4], (_Float16)y[5],
+                                                                           (_Float16)y[6], (_Float16)y[7]};
+                        } else {     // O0: 8 columns of one row
+                            *reinterpret_cast<half8 *>(blk + kSegR + row * kD + col) =
+                                half8{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3],
+                                      (_Float16)y[4], (_Float16)y[5], (_Float16)y[6], (_Float16)y[7]};
+                        }
+                        continue;
+                    }
+                    if (norm) {
                         float zf[8], t8[8];
                         unpack_bf16x8(zr, zf);
 #pragma unroll
@@ -1162,8 +1231,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                         for (int e = 0; e < 8; ++e) y[e] = nw[e] * (y[e] * rstd) * (zf[e] * t8[e]);
                     }
-                    if (tt < si.T)
-                        *reinterpret_cast<uint4 *>(a.o + ((si.tok0 + tt) * a.Hv + h) * kD + sv0 + cgl * 8) =
+                    if (tt < ss.T)
+                        *reinterpret_cast<uint4 *>(a.o + ((ss.tok0 + tt) * a.Hv + h) * kD + sv0 + cgl * 8) =
                             pack_bf16x8(y);
                 }
             };
@@ -1183,7 +1252,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (vh == 0) {
                 unsigned long long mbn[NSL] = {};  // sibling words of chunk rc, requested an iteration early
                 auto mb_request = [&](int cc) __attribute__((always_inline)) {
-                    if (a.norm && cc >= 0 && cc < nch) {
+                    if (norm && cc >= 0 && cc < nch) {
 #pragma unroll
                         for (int sib = 0; sib < NSL; ++sib)
                             mbn[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + (cc % kRing)) * kC,
@@ -1195,7 +1264,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     // 1/rms of chunk rc from the siblings' words (published kLag - 1 iterations before
                     // they were requested; a word without the chunk's tag is waited for)
                     const int rc = c - 2 - kLag;
-                    if (a.norm && rc >= 0 && rc < nch) {
+                    if (norm && rc >= 0 && rc < nch) {
                         float tot = 0.0f;
 #pragma unroll
                         for (int sib = 0; sib < NSL; ++sib) {
@@ -1207,7 +1276,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         sRstd[(rc & 1) * kC + lane] = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.eps_norm);
                     }
                     // row sums of chunk c-2 over this slice's columns -> mailbox (tag c-1)
-                    if (a.norm && c >= 2 && c - 2 < nch) {
+                    if (norm && c >= 2 && c - 2 < nch) {
                         const float *src = sO + ((c - 2) % kORing) * VT + lane;
                         float ov[BV];
 #pragma unroll
@@ -1233,7 +1302,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             }
             // raw v inputs of the last three tokens -> conv state out
-            if (vh == 0 && a.conv && a.conv_state_out && lane < 3 * NCG) {
+            if (vh == 0 && a.conv && a.conv_state_out && lane < 3 * NCG && !mcol && (!SEG || seg == a.nseg - 1)) {
                 const int sidx = lane / NCG, cg = lane % NCG;
                 const int tau = si.T - 3 + sidx;
                 const int ch = 2 * a.Hk * kD + h * kD + sv0 + cg * 8;
@@ -1250,7 +1319,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // suffices and avoids an L2 write-back per item: every mailbox word is accessed only by
         // agent-scope atomics, and a slice's last mailbox read has returned (its value was used
         // before the loop's final barrier) before its count goes up.
-        if (a.norm) {
+        if (norm) {
             __shared__ unsigned int last_one;
             if (tid == 0) {
                 const unsigned int old =
@@ -1282,6 +1351,135 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// ---------------------------------------------------------------- two-level scan: the later passes
+
+struct SegArgs {
+    const float *state_in;   // [B Hv][128][128] or nullptr
+    const float *seg_state;  // [B Hv nseg][128][256]: [M | N] of every segment
+    _Float16 *seg_frag;      // [B Hv nseg][8 column tiles][4 k-steps][64 lanes][8]: start states as MFMA B operands
+    float *state_out;        // [B Hv][128][128]
+    const _Float16 *seg_out; // per (chunk slot, value head): R fragments and O0 rows (kSegBlk halves)
+    const uint16_t *z, *norm_w;
+    uint16_t *o;
+    int B, T, Hv, nch, nseg, seg_chunks, norm;
+    float eps_norm;
+};
+
+// Start states of the segments and the final state, in fp32: S_0 = state_in,
+// S_{p+1} = M_p S_p + N_p (each segment's map is affine in its start state).  One
+// workgroup per (head, 16-column slice): the columns of a state never mix.  The start
+// state of every segment is also written as MFMA operand fragments for the output pass.
+// grid (B Hv 8), 256 threads
+__global__ __launch_bounds__(256) void seg_combine_kernel(SegArgs a) {
+    __shared__ float sS[kD][16 + 1];
+    const int chain = blockIdx.x / kTiles, ct = blockIdx.x % kTiles;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < kD * 16; i += 256) {
+        const int r = i / 16, j = i % 16;
+        sS[r][j] = a.state_in ? a.state_in[((size_t)chain * kD + r) * kD + 16 * ct + j] : 0.0f;
+    }
+    __syncthreads();
+    const int r = tid >> 1, j0 = (tid & 1) * 8;  // this thread's row and 8 columns
+    for (int p = 0; p < a.nseg; ++p) {
+        const size_t vc = (size_t)chain * a.nseg + p;
+        {   // fragment ks of column tile ct: lane L holds column l16 at rows 32 ks + {4 lq + e, 16 + 4 lq + e}
+            const int ks = tid >> 6, L = tid & 63, l16 = L & 15, lq = L >> 4;
+            half8 f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = (_Float16)sS[32 * ks + 4 * lq + e][l16];
+                f[4 + e] = (_Float16)sS[32 * ks + 16 + 4 * lq + e][l16];
+            }
+            *reinterpret_cast<half8 *>(a.seg_frag + (((vc * kTiles + ct) * 4 + ks) * 64 + L) * 8) = f;
+        }
+        const float *Mrow = a.seg_state + (vc * kD + r) * (2 * kD);
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = Mrow[kD + 16 * ct + j0 + j];
+        for (int k = 0; k < kD; k += 4) {
+            const float4 m = *reinterpret_cast<const float4 *>(Mrow + k);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[j] += m.x * sS[k][j0 + j] + m.y * sS[k + 1][j0 + j] + m.z * sS[k + 2][j0 + j] + m.w * sS[k + 3][j0 + j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sS[r][j0 + j] = acc[j];
+        __syncthreads();
+    }
+    for (int i = tid; i < kD * 16; i += 256) {
+        const int rr = i / 16, jj = i % 16;
+        a.state_out[((size_t)chain * kD + rr) * kD + 16 * ct + jj] = sS[rr][jj];
+    }
+}
+
+// Outputs of the two-level scan: O = O0 + R S_p for chunk c of segment p (R [64][128]
+// times the start state, on MFMA), then the gated RMSNorm and the bf16 store.  Wave w
+// owns rows 16 w .. 16 w + 15 of the chunk; a row's 128 columns sit in 16 lanes.  O0, z
+// and the outputs pass through LDS so that every global access is a 16-byte row piece.
+// grid (B nch Hv), 256 threads
+__global__ __launch_bounds__(256) void seg_output_kernel(SegArgs a) {
+    __shared__ _Float16 sX[kC][kD + 8];  // O0, then the bf16 outputs
+    __shared__ uint16_t sZ[kC][kD + 8];  // z
+    const int gc = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
+    const int b = gc / a.nch, c = gc % a.nch, p = c / a.seg_chunks;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
+    const size_t vc = ((size_t)b * a.Hv + h) * a.nseg + p;
+    const size_t row0 = (size_t)b * a.T + (size_t)c * kC;
+    const int nrows = min(kC, a.T - c * kC);
+    const _Float16 *blk = a.seg_out + ((size_t)gc * a.Hv + h) * kSegBlk;
+    for (int i = tid; i < kC * 16; i += 256) {
+        const int row = i >> 4, c8 = (i & 15) * 8;
+        *reinterpret_cast<half8 *>(&sX[row][c8]) = *reinterpret_cast<const half8 *>(blk + kSegR + row * kD + c8);
+        if (a.norm)
+            *reinterpret_cast<uint4 *>(&sZ[row][c8]) =
+                row < nrows ? *reinterpret_cast<const uint4 *>(a.z + ((row0 + row) * a.Hv + h) * kD + c8)
+                            : make_uint4(0, 0, 0, 0);
+    }
+    half8 A[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) A[ks] = *reinterpret_cast<const half8 *>(blk + ((w * 4 + ks) * 64 + lane) * 8);
+    floatx4 acc[8];
+    const half8 *fr = reinterpret_cast<const half8 *>(a.seg_frag) + vc * kTiles * 4 * 64 + lane;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc[ct] = mfma16x16x32(A[ks], fr[(ct * 4 + ks) * 64], acc[ct]);
+    }
+    __syncthreads();
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = 16 * w + 4 * lq + e;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            acc[ct][e] += (float)sX[row][16 * ct + l16];
+            ss[e] += acc[ct][e] * acc[ct][e];
+        }
+    }
+    __syncthreads();  // sX is reused for the outputs
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int row = 16 * w + 4 * lq + e;
+        const float rstd = __builtin_amdgcn_rsqf(group_sum<16>(ss[e]) * (1.0f / kD) + a.eps_norm);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            const int col = 16 * ct + l16;
+            float y = acc[ct][e];
+            if (a.norm) y = bf16_to_f32(a.norm_w[col]) * (y * rstd) * silu(bf16_to_f32(sZ[row][col]));
+            reinterpret_cast<uint16_t *>(&sX[row][0])[col] = f32_to_bf16(y);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < kC * 16; i += 256) {
+        const int row = i >> 4, c8 = (i & 15) * 8;
+        if (row < nrows)
+            *reinterpret_cast<uint4 *>(a.o + ((row0 + row) * a.Hv + h) * kD + c8) =
+                *reinterpret_cast<const uint4 *>(&sX[row][c8]);
+    }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct ChainLaunch {
@@ -1292,11 +1490,14 @@ struct ChainLaunch {
 
 // Compute units left to the prep kernel before it may run beside the sequential pass.
 constexpr int kPrepCUs = 16;
+// Two-level scan planning: the chip's compute units (MI355X) and the shortest segment.
+constexpr int kSegChipCUs = 256;
+constexpr int kSegMinChunks = 16;
 
-template <int NT>
+template <int NT, bool SEG>
 int chain_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
     constexpr size_t lds = ChainLds<NT>::bytes;
-    auto fn = chain_kernel<NT>;
+    auto fn = chain_kernel<NT, SEG>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds);
     if (e != hipSuccess) return fail("hipFuncSetAttribute(chain_kernel)", e);
@@ -1307,7 +1508,7 @@ int chain_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn), 512, lds)) !=
         hipSuccess)
         return fail("hipOccupancyMaxActiveBlocksPerMultiprocessor(chain_kernel)", e);
-    constexpr int NSL = kTiles / NT;
+    constexpr int NSL = (SEG ? 2 : 1) * kTiles / NT;
     // One workgroup per resident slot at most: a workgroup that waits for its
     // sibling slices holds its slot, and the ticket order lets the next free
     // slot start them.  At least 8 * NSL slots keep a started slice of every
@@ -1337,7 +1538,33 @@ int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan) {
     plan->ready_bytes = align256((size_t)plan->nslots * Hk * sizeof(unsigned int));
     plan->mbox_bytes = align256((size_t)chains * kTiles * kRing * kC * sizeof(unsigned long long)) +
                        align256((size_t)chains * sizeof(unsigned int)) + 256;
-    plan->total_bytes = plan->qk_bytes + plan->tp_bytes + plan->ready_bytes + plan->mbox_bytes;
+    // Two-level scan (even batches): worth it when the sequential pass would leave most of
+    // the chip idle (few heads) and the sequences are long.  Its first pass runs 256 columns
+    // per head, so nseg segments keep about B Hv 16 nseg workgroups busy.  The environment
+    // variable GDN_PREFILL_SEGMENTS overrides the choice (0 or 1: never, n >= 2: n segments).
+    plan->nseg = 1;
+    plan->seg_chunks = plan->nchunks;
+    if (!packed) {
+        long long want = 0;
+        if (const char *e = std::getenv("GDN_PREFILL_SEGMENTS"))
+            want = std::atoll(e);
+        else if (chains * nsl * 4 <= kSegChipCUs)  // the sequential pass would use at most a quarter of the chip
+            want = std::min<long long>(kSegChipCUs / (chains * 16), plan->nchunks / kSegMinChunks);
+        want = std::min<long long>(want, plan->nchunks);
+        if (want >= 2) {
+            plan->seg_chunks = (int)((plan->nchunks + want - 1) / want);
+            plan->nseg = (plan->nchunks + plan->seg_chunks - 1) / plan->seg_chunks;
+        }
+    }
+    plan->seg_out_bytes = plan->seg_state_bytes = plan->seg_frag_bytes = 0;
+    if (plan->nseg > 1) {
+        const size_t vchains = (size_t)chains * plan->nseg;
+        plan->seg_out_bytes = align256((size_t)B * plan->nchunks * Hv * kSegBlk * sizeof(_Float16));
+        plan->seg_state_bytes = align256(vchains * kD * 2 * kD * sizeof(float));
+        plan->seg_frag_bytes = align256(vchains * kTiles * 4 * kFrag * sizeof(_Float16));
+    }
+    plan->total_bytes = plan->qk_bytes + plan->tp_bytes + plan->ready_bytes + plan->mbox_bytes +
+                        plan->seg_out_bytes + plan->seg_state_bytes + plan->seg_frag_bytes;
     return 0;
 }
 
@@ -1390,7 +1617,10 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     _Float16 *qkf = reinterpret_cast<_Float16 *>(ws);
     _Float16 *tpf = reinterpret_cast<_Float16 *>(ws + plan.qk_bytes);
     unsigned int *ready = reinterpret_cast<unsigned int *>(ws + plan.qk_bytes + plan.tp_bytes);
-    unsigned char *mb = ws + plan.qk_bytes + plan.tp_bytes + plan.ready_bytes;
+    // the two-level scan's regions (if any), then the exchange area, whose last 256 bytes hold
+    // the error word at the very end of the workspace
+    unsigned char *sgb = ws + plan.qk_bytes + plan.tp_bytes + plan.ready_bytes;
+    unsigned char *mb = sgb + plan.seg_out_bytes + plan.seg_state_bytes + plan.seg_frag_bytes;
     const size_t chains = (size_t)p.B * p.Hv;
     const size_t mbox_sz = align256(chains * kTiles * kRing * kC * sizeof(unsigned long long));
     unsigned int *counters = reinterpret_cast<unsigned int *>(mb + mbox_sz);
@@ -1420,9 +1650,16 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     a.nch = plan.nchunks; a.n_items = (int)(chains * plan.nslice); a.grid = 0;
     a.eps_norm = p.eps_norm;
 
+    const bool seg = plan.nseg > 1;
+    a.seg_out = seg ? reinterpret_cast<_Float16 *>(sgb) : nullptr;
+    a.seg_state = seg ? reinterpret_cast<float *>(sgb + plan.seg_out_bytes) : nullptr;
+    a.nseg = plan.nseg; a.seg_chunks = plan.seg_chunks;
+    if (seg) a.n_items = (int)(chains * plan.nseg * 2 * plan.nslice);
+
     ChainLaunch cl;
-    int rc = plan.nt == 1 ? chain_launch_shape<1>(a, &cl) : plan.nt == 2 ? chain_launch_shape<2>(a, &cl)
-                                                                         : fail("prefill plan: unsupported value-tile count");
+    int rc = plan.nt == 1 ? (seg ? chain_launch_shape<1, true>(a, &cl) : chain_launch_shape<1, false>(a, &cl))
+             : plan.nt == 2 ? (seg ? chain_launch_shape<2, true>(a, &cl) : chain_launch_shape<2, false>(a, &cl))
+                            : fail("prefill plan: unsupported value-tile count");
     if (rc) return rc;
     a.grid = cl.grid;
 
@@ -1431,7 +1668,8 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     // finishes); otherwise the two run one after the other on the caller's stream.
     // Prep is enqueued first either way: if both streams share a hardware queue,
     // the sequential pass simply starts after it.
-    const bool beside = cl.grid + kPrepCUs <= cl.ncu && beside_allowed();
+    // (The two-level scan's first pass starts every segment at once, so it runs after prep.)
+    const bool beside = !seg && cl.grid + kPrepCUs <= cl.ncu && beside_allowed();
     hipStream_t ps = stream;
     SideStream *ss = nullptr;
     std::unique_lock<std::mutex> lock;
@@ -1462,6 +1700,22 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     void *cargs[] = {&a};
     if ((e = hipLaunchKernel(cl.fn, dim3(cl.grid), dim3(512), cargs, cl.lds, stream)) != hipSuccess)
         return fail("hipLaunchKernel(chain_kernel)", e);
+    if (seg) {
+        SegArgs sa;
+        sa.state_in = p.state_in; sa.seg_state = a.seg_state;
+        sa.seg_frag = reinterpret_cast<_Float16 *>(sgb + plan.seg_out_bytes + plan.seg_state_bytes);
+        sa.state_out = p.state_out; sa.seg_out = a.seg_out; sa.z = p.z; sa.norm_w = p.norm_w; sa.o = p.o;
+        sa.B = p.B; sa.T = p.T; sa.Hv = p.Hv; sa.nch = plan.nchunks; sa.nseg = plan.nseg;
+        sa.seg_chunks = plan.seg_chunks; sa.norm = p.norm; sa.eps_norm = p.eps_norm;
+        void *sargs[] = {&sa};
+        if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_combine_kernel), dim3((unsigned)(chains * kTiles)),
+                                 dim3(256), sargs, 0, stream)) != hipSuccess)
+            return fail("hipLaunchKernel(seg_combine_kernel)", e);
+        if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_output_kernel),
+                                 dim3((unsigned)((size_t)p.B * plan.nchunks * p.Hv)), dim3(256), sargs, 0, stream)) !=
+            hipSuccess)
+            return fail("hipLaunchKernel(seg_output_kernel)", e);
+    }
     // the caller's stream completes only after both kernels
     if (beside && (e = hipStreamWaitEvent(stream, ss->done, 0)) != hipSuccess) return fail("hipStreamWaitEvent", e);
     return 0;
