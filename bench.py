@@ -9,7 +9,9 @@ Prints ONE JSON line.  `value` is prefill tokens/s of the layer.  Extra fields
 carry the roofline of the timed call, the decode step on the 27B-shaped
 B=256 workload (state GB/s, % of HBM) and the same batch checking two tokens per
 sequence with snapshots, the other prefill shapes, the 4B-shaped
-layer's tokens as 16 packed sequences of mixed lengths, and the fp64
+layer's tokens as 16 packed sequences of mixed lengths, one GPU's share of the
+27B-shaped layer under 16-way key-head sharding (the two-level scan beside the
+plain sequential pass), and the fp64
 CPU oracle timed on this host (a reported baseline, not a target).
 
 Inputs are synthetic and seeded (torch's generator on the GPU for the timed
@@ -210,6 +212,44 @@ def bench_prefill_packed(torch, gdn, steps, warmup):
     return res
 
 
+# one GPU's share of the 27B-shaped layer under 16-way key-head sharding: 1 key head, its 3 value heads
+SHARD = ("qwen38_27b_prefill_T262144_keyhead_shard_1of16", (1, 262144, 1, 3))
+
+
+def bench_prefill_shard(torch, gdn, steps, warmup):
+    """The few-heads, long-sequence shape the two-level scan is for, timed as the library
+    plans it (segments) and, for comparison, with the plain sequential pass
+    (GDN_PREFILL_SEGMENTS=0)."""
+    name, (B, T, Hk, Hv) = SHARD
+    out = {"workload": name, "B": B, "T": T, "Hk": Hk, "Hv": Hv}
+    old = os.environ.get("GDN_PREFILL_SEGMENTS")
+    try:
+        for leg, env in (("plain_sequential", "0"), ("planned", None)):
+            if env is None:
+                os.environ.pop("GDN_PREFILL_SEGMENTS", None)
+            else:
+                os.environ["GDN_PREFILL_SEGMENTS"] = env
+            d = make_prefill_set(torch, gdn, B, T, Hk, Hv, seed=1200)
+            torch.cuda.synchronize()
+            ms, _ = time_calls(torch, lambda dd: run_prefill(gdn, dd), [d], steps, warmup)
+            out[leg + "_ms_per_call"] = ms
+            out[leg + "_workspace_MiB"] = d["ws"].numel() / 2 ** 20
+            del d
+            torch.cuda.empty_cache()
+    finally:
+        if old is None:
+            os.environ.pop("GDN_PREFILL_SEGMENTS", None)
+        else:
+            os.environ["GDN_PREFILL_SEGMENTS"] = old
+    ms = out["planned_ms_per_call"]
+    nbytes = prefill_bytes(B, T, Hk, Hv)
+    flops = USEFUL_FLOP_PER_TOKEN_HEAD * B * T * Hv
+    out.update(tokens_per_s=B * T / (ms * 1e-3), algorithmic_bytes=nbytes, hbm_frac=nbytes / (ms * 1e-3) / HBM_PEAK,
+               mfma_useful_frac=flops / (ms * 1e-3) / MFMA_FP16_PEAK,
+               speedup_over_plain=out["plain_sequential_ms_per_call"] / ms, steps=steps)
+    return out
+
+
 def bench_decode(torch, gdn, steps, warmup):
     B, Hk, Hv = DECODE[1]
     gen = torch.Generator(device="cuda")
@@ -391,6 +431,8 @@ def main(argv=None):
                 B, T, Hk, Hv = WORKLOADS[name]
                 steps = max(3, min(args.steps, int(2e8 // (B * T * Hv))))
                 extra[name] = bench_prefill(torch, gdn, name, steps, 2)
+        # few heads, long sequence: the two-level scan against the plain sequential pass
+        extra[SHARD[0]] = bench_prefill_shard(torch, gdn, 5, 1)
         # the 4B-shaped layer's tokens as packed sequences of mixed lengths
         extra[PACKED[0]] = bench_prefill_packed(torch, gdn, 20, 2)
         # the same layer through the entry point that takes the gate logits

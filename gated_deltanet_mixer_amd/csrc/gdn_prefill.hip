@@ -1540,8 +1540,11 @@ int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan) {
                        align256((size_t)chains * sizeof(unsigned int)) + 256;
     // Two-level scan (even batches): worth it when the sequential pass would leave most of
     // the chip idle (few heads) and the sequences are long.  Its first pass runs 256 columns
-    // per head, so nseg segments keep about B Hv 16 nseg workgroups busy.  The environment
-    // variable GDN_PREFILL_SEGMENTS overrides the choice (0 or 1: never, n >= 2: n segments).
+    // per head in slices of 32 (measured on the shapes it is for: as many 32-column slices
+    // as fit the chip beat half as many segments in 16-column slices, at about 2 us against
+    // 1.25 us per chunk), so nseg segments keep B Hv 8 nseg workgroups busy; nseg fills one
+    // round of the chip.  The environment variable GDN_PREFILL_SEGMENTS overrides the
+    // choice (0 or 1: never, n >= 2: n segments).
     plan->nseg = 1;
     plan->seg_chunks = plan->nchunks;
     if (!packed) {
@@ -1549,11 +1552,14 @@ int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan) {
         if (const char *e = std::getenv("GDN_PREFILL_SEGMENTS"))
             want = std::atoll(e);
         else if (chains * nsl * 4 <= kSegChipCUs)  // the sequential pass would use at most a quarter of the chip
-            want = std::min<long long>(kSegChipCUs / (chains * 16), plan->nchunks / kSegMinChunks);
+            want = std::min<long long>(kSegChipCUs / (chains * 8), plan->nchunks / kSegMinChunks);
         want = std::min<long long>(want, plan->nchunks);
         if (want >= 2) {
             plan->seg_chunks = (int)((plan->nchunks + want - 1) / want);
             plan->nseg = (plan->nchunks + plan->seg_chunks - 1) / plan->seg_chunks;
+            plan->nslice = 4;  // 32-column slices in the segment pass
+            plan->nt = 2;
+            plan->bv = 32;
         }
     }
     plan->seg_out_bytes = plan->seg_state_bytes = plan->seg_frag_bytes = 0;
