@@ -101,6 +101,15 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
  * blocks of 64 tokens ("How Qwen3.5 works" §9.11: the unit lower-triangular
  * chunk form of the same recurrence; a partial last chunk is allowed).
  *
+ * With few (sequence, value head) pairs and long sequences the library splits
+ * each sequence into segments that run at the same time: a segment's effect on
+ * the state is affine in its start state (the chunk form's update is linear in
+ * S), so each segment is run from zero together with its transition map, the
+ * maps are chained, and what each start state adds to the outputs is applied
+ * last.  The workspace is then larger (gdn_prefill_workspace_size accounts for
+ * it).  The environment variable GDN_PREFILL_SEGMENTS, read at every call,
+ * overrides the choice: 0 or 1 never splits, n >= 2 asks for n segments.
+ *
  *  q, k           [B][T][Hk][128] bf16
  *  v, z           [B][T][Hv][128] bf16 (z may be NULL iff GDN_NO_NORM)
  *  g, beta        [B][T][Hv] fp32: log-decay (alpha = e^g) and write strength
