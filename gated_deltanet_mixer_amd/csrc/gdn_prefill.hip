@@ -145,13 +145,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // still runs: written through to memory (agent-coherent, the encoding of an
 // agent-scope relaxed atomic store), so a block can publish its stamp after its
 // stores complete without writing back a whole L2.
+// Workspace stores of the prep kernel: written through to memory (sc1) when the sequential
+// pass may read them while the prep kernel still runs, ordinary stores otherwise (the
+// kernel boundary then orders them).
 constexpr int kWriteThrough = 16;  // sc1
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st_through(__amdgpu_buffer_rsrc_t r, int voff, half8 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, kWriteThrough);
+template <bool THROUGH>
+__device__ __forceinline__ void st_ws(__amdgpu_buffer_rsrc_t r, int voff, half8 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, THROUGH ? kWriteThrough : 0);
 }
-__device__ __forceinline__ void st_through(__amdgpu_buffer_rsrc_t r, int voff, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, kWriteThrough);
+template <bool THROUGH>
+__device__ __forceinline__ void st_ws(__amdgpu_buffer_rsrc_t r, int voff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, THROUGH ? kWriteThrough : 0);
 }
 
 // 4 fp16 from LDS through the transposing read: within each 16-lane group the
@@ -238,6 +243,8 @@ struct PrepLds {
 };
 
 // grid (slots * Hk), 256 threads: slot b nch + c of an even batch, else where seq_info places it
+// THROUGH: the sequential pass runs at the same time and follows the ready stamps.
+template <bool THROUGH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_prep_kernel(PrepArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + PrepLds::sQ);
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const int ff = f & 15;
             const _Float16 *src = M + (16 * (ff >> 2) + fl) * P128 + 32 * (ff & 3) + 4 * fq;
             const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
-            st_through(rq, idx * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            st_ws<THROUGH>(rq, idx * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         }
     }
 
@@ -461,9 +468,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const float gc = __shfl(gv, 63, 64);
             sG[lane] = gv;
             sB[lane] = bv;
-            st_through(rtp, kVecOff * 2 + 4 * lane, __expf(gv));
-            st_through(rtp, kVecOff * 2 + 4 * (kC + lane), __expf(gc - gv));
-            if (lane < 4) st_through(rtp, kVecOff * 2 + 4 * (2 * kC + lane), __expf(gc));
+            st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * lane, __expf(gv));
+            st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * (kC + lane), __expf(gc - gv));
+            if (lane < 4) st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * (2 * kC + lane), __expf(gc));
         }
         lds_barrier();
 
@@ -490,16 +497,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
         lds_barrier();
 
-        // diagonal 16x16 blocks of T = (I + L)^{-1}: forward substitution, one column per lane
+        // diagonal 16x16 blocks of T = (I + L)^{-1}: forward substitution, one column per lane,
+        // column-oriented (once x[mm] is final it is subtracted from every later row at once),
+        // so the dependent steps are the 15 rows rather than every product; the products and
+        // their order per row are those of the row-by-row form
         if (lane < 16) {
             const int w0 = 16 * wave, cidx = lane;
             float x[16];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                float acc = 0.0f;
+            for (int rr = 0; rr < 16; ++rr) x[rr] = rr == cidx ? 1.0f : 0.0f;
 #pragma unroll
-                for (int mm = 0; mm < rr; ++mm) acc += sL[(w0 + rr) * PL + w0 + mm] * x[mm];
-                x[rr] = (rr == cidx) ? 1.0f : (rr < cidx ? 0.0f : -acc);
+            for (int mm = 0; mm < 15; ++mm) {
+                const float xm = x[mm];
+#pragma unroll
+                for (int rr = mm + 1; rr < 16; ++rr) x[rr] -= sL[(w0 + rr) * PL + w0 + mm] * xm;
             }
             const float bc = sB[w0 + cidx];
             const int db = wave * (wave + 1) / 2 + wave;
@@ -575,13 +586,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }
-            st_through(rtp, ((f < 6 ? 0 : kPOff - 6 * kFrag) + idx * 8) * 2, v);
+            st_ws<THROUGH>(rtp, ((f < 6 ? 0 : kPOff - 6 * kFrag) + idx * 8) * 2, v);
         }
         lds_barrier();
     }
-    // every wave's (written-through) stores complete, then the block's stamp
-    wait_vmcnt<0>();
-    __syncthreads();
+    // every wave's (written-through) stores complete, then the block's stamp; with the
+    // sequential pass waiting for this kernel to end, the stamp needs no ordering
+    if (THROUGH) {
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
     if (tid == 0)
         __hip_atomic_store(a.ready + (size_t)gc * a.Hk + kh, a.stamp, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -1488,26 +1502,62 @@ struct ChainLaunch {
     int grid, ncu;
 };
 
-// Compute units left to the prep kernel before it may run beside the sequential pass.
+// Compute units left to the prep kernel before it may run beside the sequential pass, and
+// the shortest sequence (in chunks) for which it does.
 constexpr int kPrepCUs = 16;
+constexpr int kBesideMinChunks = 32;
 // Two-level scan planning: the chip's compute units (MI355X) and the shortest segment.
 constexpr int kSegChipCUs = 256;
 constexpr int kSegMinChunks = 16;
+
+// What a launch needs to know about a device and a kernel, found on first use and kept
+// (the queries cost tens of microseconds of host time per call otherwise).
+struct DeviceFacts {
+    std::mutex mu;
+    int ncu = 0;
+    int chain_per_cu[2][2] = {{0, 0}, {0, 0}};  // [NT - 1][SEG]: resident chain workgroups per CU
+    int prep_lds[2] = {0, 0};                   // [THROUGH]: dynamic LDS limit set for the prep kernel
+};
+
+int device_facts(DeviceFacts **out) {
+    static DeviceFacts per_dev[64];
+    int dev = 0;
+    hipError_t e;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return fail("hipGetDevice", e);
+    if (dev < 0 || dev >= 64) return fail("prefill: device index out of range");
+    *out = &per_dev[dev];
+    return 0;
+}
 
 template <int NT, bool SEG>
 int chain_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
     constexpr size_t lds = ChainLds<NT>::bytes;
     auto fn = chain_kernel<NT, SEG>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return fail("hipFuncSetAttribute(chain_kernel)", e);
-    int dev = 0, ncu = 0, per_cu = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return fail("hipGetDevice", e);
-    if ((e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
-        return fail("hipDeviceGetAttribute(multiprocessor count)", e);
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(fn), 512, lds)) !=
-        hipSuccess)
-        return fail("hipOccupancyMaxActiveBlocksPerMultiprocessor(chain_kernel)", e);
+    DeviceFacts *df;
+    int rc = device_facts(&df);
+    if (rc) return rc;
+    int ncu, per_cu;
+    {
+        std::lock_guard<std::mutex> g(df->mu);
+        hipError_t e;
+        if (!df->ncu) {
+            int dev = 0;
+            if ((e = hipGetDevice(&dev)) != hipSuccess) return fail("hipGetDevice", e);
+            if ((e = hipDeviceGetAttribute(&df->ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+                return fail("hipDeviceGetAttribute(multiprocessor count)", e);
+        }
+        int &pc = df->chain_per_cu[NT - 1][SEG ? 1 : 0];
+        if (!pc) {
+            if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds)) != hipSuccess)
+                return fail("hipFuncSetAttribute(chain_kernel)", e);
+            if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, reinterpret_cast<const void *>(fn), 512, lds)) !=
+                hipSuccess)
+                return fail("hipOccupancyMaxActiveBlocksPerMultiprocessor(chain_kernel)", e);
+        }
+        ncu = df->ncu;
+        per_cu = pc;
+    }
     constexpr int NSL = (SEG ? 2 : 1) * kTiles / NT;
     // One workgroup per resident slot at most: a workgroup that waits for its
     // sibling slices holds its slot, and the ticket order lets the next free
@@ -1674,8 +1724,10 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     // finishes); otherwise the two run one after the other on the caller's stream.
     // Prep is enqueued first either way: if both streams share a hardware queue,
     // the sequential pass simply starts after it.
-    // (The two-level scan's first pass starts every segment at once, so it runs after prep.)
-    const bool beside = !seg && cl.grid + kPrepCUs <= cl.ncu && beside_allowed();
+    // (The two-level scan's first pass starts every segment at once, so it runs after prep.
+    // Short sequences run one kernel after the other too: the overlap then saves less than
+    // the two events and stream waits it costs on the host.)
+    const bool beside = !seg && plan.nchunks >= kBesideMinChunks && cl.grid + kPrepCUs <= cl.ncu && beside_allowed();
     hipStream_t ps = stream;
     SideStream *ss = nullptr;
     std::unique_lock<std::mutex> lock;
@@ -1694,11 +1746,21 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
         ps = ss->s;
     }
     const size_t plds = PrepLds::bytes(pa.r);
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_prep_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds)) != hipSuccess)
-        return fail("hipFuncSetAttribute(chunk_prep_kernel)", e);
+    const void *prep_fn = beside ? reinterpret_cast<const void *>(chunk_prep_kernel<true>)
+                                 : reinterpret_cast<const void *>(chunk_prep_kernel<false>);
+    {   // raise the prep kernel's LDS limit when this head ratio needs more than set so far
+        DeviceFacts *df;
+        if ((rc = device_facts(&df))) return rc;
+        std::lock_guard<std::mutex> g(df->mu);
+        int &lim = df->prep_lds[beside ? 1 : 0];
+        if ((int)plds > lim) {
+            if ((e = hipFuncSetAttribute(prep_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds)) != hipSuccess)
+                return fail("hipFuncSetAttribute(chunk_prep_kernel)", e);
+            lim = (int)plds;
+        }
+    }
     void *pargs[] = {&pa};
-    if ((e = hipLaunchKernel(reinterpret_cast<const void *>(chunk_prep_kernel),
+    if ((e = hipLaunchKernel(prep_fn,
                              dim3((unsigned)(plan.nslots * p.Hk)), dim3(256), pargs, plds, ps)) !=
         hipSuccess)
         return fail("hipLaunchKernel(chunk_prep_kernel)", e);
