@@ -619,7 +619,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 constexpr int kLag = 3;
 constexpr int kRing = 8;           // mailbox slots: chunks c-2-kLag .. c+kLag-2 can be live
 constexpr int kORing = kLag + 3;   // pre-norm output tiles in LDS
-constexpr int kDma = 3;            // operand slots: chunk c+2 loads while chunk c is used
+// How far ahead the load wave works is set per tile count (ChainLds::D): a DMA issued in
+// iteration j is waited for at the end of iteration j + D - 1 and used from j + D + 1 on.
 static_assert(kRing >= 2 * kLag + 1, "mailbox depth");
 
 struct ChainArgs {
@@ -635,6 +636,7 @@ struct ChainArgs {
     unsigned int *exits;       // workgroups that have left the item loop
     const unsigned int *ready; // [slots][Hk] prep stamps
     unsigned int stamp;
+    int check;                 // the prep kernel may still be running: follow the stamps
     const int *cu;             // packed sequences: [B + 1] token offsets (nullptr: even batch)
     // segment pass (two-level scan): segments of seg_chunks chunks, nseg per sequence
     _Float16 *seg_out;         // per (chunk slot, value head) kSegBlk halves: R as MFMA A fragments, O0 rows
@@ -651,13 +653,17 @@ template <int NT>
 struct ChainLds {
     static constexpr int BV = 16 * NT;
     static constexpr int VT = BV * PL;                          // floats of one column-major [BV][64] tile
-    static constexpr size_t sOp = 0;                             // [kDma][kOpSlot]       DMA'd operands
-    static constexpr size_t sSD = sOp + (size_t)kDma * kOpSlot;  // [2][NT][kSD]         Sb, Db fragments per tile
+    // DMA lead in iterations: 2 where the LDS has room for the extra slots (one 16-column
+    // tile), else 1.  The operand, raw-v and z rings hold D + 2 chunks each.
+    static constexpr int D = NT == 1 ? 2 : 1;
+    static constexpr int NSLOT = D + 2;
+    static constexpr size_t sOp = 0;                             // [NSLOT][kOpSlot]     DMA'd operands
+    static constexpr size_t sSD = sOp + (size_t)NSLOT * kOpSlot; // [2][NT][kSD]         Sb, Db fragments per tile
     static constexpr size_t sV = sSD + 2 * NT * kSD;             // fp16 [2][BV][P64]     conv(v) of the slice
     static constexpr size_t sO = sV + 2 * 2 * BV * P64;          // fp32 [kORing][BV][PL] pre-norm output
-    static constexpr size_t sRawV = sO + 4 * kORing * VT;        // bf16 [3][64][BV]      raw v
-    static constexpr size_t sZ = sRawV + 2 * 3 * kC * BV;        // bf16 [3][64][BV]      z
-    static constexpr size_t sHalo = sZ + 2 * 3 * kC * BV;        // bf16 [2][3][BV]       raw v rows before a chunk
+    static constexpr size_t sRawV = sO + 4 * kORing * VT;        // bf16 [NSLOT][64][BV]  raw v
+    static constexpr size_t sZ = sRawV + 2 * NSLOT * kC * BV;    // bf16 [NSLOT][64][BV]  z
+    static constexpr size_t sHalo = sZ + 2 * NSLOT * kC * BV;    // bf16 [2][3][BV]       raw v rows before a chunk
     static constexpr size_t sRstd = sHalo + 2 * 2 * 3 * BV;      // fp32 [2][64]          gated-norm 1/rms
     static constexpr size_t sCW = sRstd + 4 * 2 * kC;            // fp32 [BV][4]          conv taps of the v channels
     static constexpr size_t sNW = sCW + 4 * 4 * BV;              // fp32 [BV]             gated-norm weights
@@ -702,7 +708,7 @@ template <int NT>
 __device__ __forceinline__ void state_step(unsigned char *smem, floatx4 (&S)[8], StateFrags &fr,
                                            const _Float16 *tpn, int c, int t, int lane, int jc, int lq, int trofs) {
     using L = ChainLds<NT>;
-    const unsigned char *op = smem + L::sOp + (c % kDma) * kOpSlot;
+    const unsigned char *op = smem + L::sOp + (c % L::NSLOT) * kOpSlot;
     const _Float16 *opk = reinterpret_cast<const _Float16 *>(op);
     const _Float16 *sVc = reinterpret_cast<const _Float16 *>(smem + L::sV) + (c & 1) * L::BV * P64;
     half8 *sd = reinterpret_cast<half8 *>(smem + L::sSD + ((c & 1) * NT + t) * kSD) + lane;
@@ -843,7 +849,8 @@ __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, u
     return w;
 }
 
-__device__ __forceinline__ int mod3(int x) { return ((x % 3) + 3) % 3; }
+template <int N>
+__device__ __forceinline__ int modn(int x) { return ((x % N) + N) % N; }
 
 // Two-level scan: what the first pass hands the last one per (chunk slot, value head), in fp16:
 // R [64][128] (the read-out of the transition columns) as 16 MFMA A-operand fragments
@@ -865,8 +872,10 @@ __device__ __forceinline__ const unsigned int *ready_word(const ChainArgs &a, in
 __device__ __forceinline__ bool stamp_ok(const ChainArgs &a, unsigned int w) { return (int)(w - a.stamp) >= 0; }
 
 // Wait until the prep block is complete.  Bounded like every cross-workgroup
-// wait: on a timeout the error word is raised.
+// wait: on a timeout the error word is raised.  With the prep kernel finished
+// before this one started (a.check == 0) there is nothing to wait for.
 __device__ __forceinline__ void wait_ready(const ChainArgs &a, int gc, int kh, int &broken) {
+    if (!a.check) return;
     const unsigned int *f = ready_word(a, gc, kh);
     uint32_t n = 0;
     while (!stamp_ok(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
@@ -1067,19 +1076,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             };
             auto ops_dma = [&](int cc) __attribute__((always_inline)) {
                 const int cl = min(cc, nch - 1);  // (past the last chunk: a harmless duplicate)
-                unsigned char *slot = smem + L::sOp + (cc % kDma) * kOpSlot;
+                unsigned char *slot = smem + L::sOp + (cc % L::NSLOT) * kOpSlot;
                 const _Float16 *kb = qk0 + cl * qk_stride + kKOff;
 #pragma unroll
                 for (int f = 0; f < 16; ++f) dma16(kb + f * kFrag + kswz(lane) * 8, slot + f * 1024);
             };
             const uint16_t *zsrc = norm ? a.z : a.v;
-            // prologue: operands of chunks 0 and 1, raw v of chunks 0..2.  The load wave is
-            // the one that waits for the prep blocks: A and B load a chunk's operands only
-            // after the barrier that follows its wait.
-            wait_ready(a, sc0, kh, broken);
-            if (nch > 1) wait_ready(a, sc0 + 1, kh, broken);
-            ops_dma(0);
-            ops_dma(1);
+            // prologue: operands of chunks 0..D, raw v of chunks 0..D+1.  The load wave is the
+            // one that waits for the prep blocks: A and B load a chunk's operands only after the
+            // barrier that follows its wait.
+            if (a.check) {  // chunks 0..D: all stamps requested at once, one memory round trip
+                unsigned int w[L::D + 1];
+#pragma unroll
+                for (int j = 0; j <= L::D; ++j)
+                    w[j] = __hip_atomic_load(ready_word(a, sc0 + min(j, nch - 1), kh), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int j = 0; j <= L::D; ++j)
+                    if (j < nch && !stamp_ok(a, w[j])) wait_ready(a, sc0 + j, kh, broken);
+            }
+#pragma unroll
+            for (int j = 0; j <= L::D; ++j) ops_dma(j);
             // a chunk's stamp is requested two iterations before it is needed, so that waiting
             // for the previous iteration's DMA group never waits for a stamp load as well.  The
             // load is issued in every iteration, past the last chunk from the last chunk's word
@@ -1097,10 +1114,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             };
             // two stamp registers used in turn (iteration c reads and refills the one of its
             // parity), so no in-flight load is ever copied between registers
-            unsigned int stamp_e = stamp_load(2), stamp_o = stamp_load(3);  // chunk c+2 for even / odd c
-            rows_dma(a.v, 0, sRawV);
-            rows_dma(a.v, 1, sRawV + kC * BV);
-            rows_dma(a.v, 2, sRawV + 2 * kC * BV);
+            unsigned int stamp_e = stamp_load(1 + L::D), stamp_o = stamp_load(2 + L::D);  // chunk c+1+D, even / odd c
+#pragma unroll
+            for (int j = 0; j <= L::D + 1; ++j) rows_dma(a.v, j, sRawV + j * kC * BV);
             wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_s_barrier();
@@ -1108,15 +1124,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // (kept in program order: a stamp test moved into the previous iteration's DMA
                 // group would make the wave wait for that whole group)
                 __builtin_amdgcn_sched_barrier(0);
-                // this iteration's group: operands of chunk c+2, raw v of chunk c+3, z of chunk c-1-kLag
-                if (c + 2 < nch && !stamp_ok(a, st)) wait_ready(a, sc0 + c + 2, kh, broken);
-                st = stamp_load(c + 4);
-                ops_dma(c + 2);
-                rows_dma(a.v, c + 3, sRawV + mod3(c + 3) * kC * BV);
-                rows_dma(zsrc, c - 1 - kLag, sZ + mod3(c - 1 - kLag) * kC * BV);
-                // the previous iteration's group (chunk c+1) has landed (this iteration's stamp
-                // load and group may still be in flight)
-                wait_vmcnt<GROUP + 1>();
+                // this iteration's group: operands of chunk c+1+D, raw v of chunk c+2+D, z of
+                // chunk c-2-kLag+D
+                if (a.check && c + 1 + L::D < nch && !stamp_ok(a, st)) wait_ready(a, sc0 + c + 1 + L::D, kh, broken);
+                st = stamp_load(c + 3 + L::D);
+                ops_dma(c + 1 + L::D);
+                rows_dma(a.v, c + 2 + L::D, sRawV + modn<L::NSLOT>(c + 2 + L::D) * kC * BV);
+                rows_dma(zsrc, c - 2 - kLag + L::D, sZ + modn<L::NSLOT>(c - 2 - kLag + L::D) * kC * BV);
+                // the group of iteration c+1-D has landed (the last D groups, stamp loads
+                // included, may still be in flight)
+                wait_vmcnt<L::D * (GROUP + 1)>();
                 __builtin_amdgcn_s_barrier();
             };
             int c = 0;
@@ -1159,12 +1176,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             auto conv_v = [&](int cc) __attribute__((always_inline)) {
                 if (vtid < kConvBase) return;  // not a converting helper
                 _Float16 *dst = sV + (cc & 1) * BV * P64 + cgl * 8 * P64;
-                const uint16_t *cur = sRawV + mod3(cc) * kC * BV + cgl * 8;
+                const uint16_t *cur = sRawV + modn<L::NSLOT>(cc) * kC * BV + cgl * 8;
                 const uint16_t *prev = sHalo + (cc & 1) * 3 * BV + cgl * 8 - (kC - 3) * BV;  // row kC+r2 -> halo row 3+r2
                 if (vtid - kConvBase >= 0 && vtid - kConvBase < 3 * NCG) {
                     const int r3 = (vtid - kConvBase) / NCG, cg = vtid % NCG;
                     *reinterpret_cast<uint4 *>(sHalo + ((cc + 1) & 1) * 3 * BV + r3 * BV + cg * 8) =
-                        *reinterpret_cast<const uint4 *>(sRawV + mod3(cc) * kC * BV + (kC - 3 + r3) * BV + cg * 8);
+                        *reinterpret_cast<const uint4 *>(sRawV + modn<L::NSLOT>(cc) * kC * BV + (kC - 3 + r3) * BV + cg * 8);
                 }
 #pragma unroll 1
                 for (int it = vtid - kConvBase; it < kC * NCG; it += kConvLanes) {
@@ -1207,7 +1224,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             auto gate = [&](int oc) __attribute__((always_inline)) {
                 const float *src = sO + (oc % kORing) * VT + cgl * 8 * PL;
                 const float *rs = sRstd + (oc & 1) * kC;
-                const uint16_t *zt = sZ + mod3(oc) * kC * BV + cgl * 8;
+                const uint16_t *zt = sZ + modn<L::NSLOT>(oc) * kC * BV + cgl * 8;
 #pragma unroll 1
                 for (int it = vtid - 64; it < kC * NCG; it += kGateLanes) {
                     const int row = it / NCG;
@@ -1701,7 +1718,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w; a.conv_state_in = p.conv_state_in;
     a.state_in = p.state_in; a.o = p.o; a.conv_state_out = p.conv_state_out; a.state_out = p.state_out;
     a.mbox = reinterpret_cast<unsigned long long *>(mb); a.counters = counters; a.err = err;
-    a.tickets = err + 16; a.exits = err + 32; a.ready = ready; a.stamp = stamp; a.cu = p.cu_seqlens;
+    a.tickets = err + 16; a.exits = err + 32; a.ready = ready; a.stamp = stamp; a.cu = p.cu_seqlens; a.check = 1;
     a.B = p.B; a.T = p.T; a.Hk = p.Hk; a.Hv = p.Hv; a.r = pa.r; a.Cc = pa.Cc; a.conv = pa.conv; a.norm = p.norm;
     a.nch = plan.nchunks; a.n_items = (int)(chains * plan.nslice); a.grid = 0;
     a.eps_norm = p.eps_norm;
@@ -1728,6 +1745,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     // Short sequences run one kernel after the other too: the overlap then saves less than
     // the two events and stream waits it costs on the host.)
     const bool beside = !seg && plan.nchunks >= kBesideMinChunks && cl.grid + kPrepCUs <= cl.ncu && beside_allowed();
+    a.check = beside ? 1 : 0;
     hipStream_t ps = stream;
     SideStream *ss = nullptr;
     std::unique_lock<std::mutex> lock;
