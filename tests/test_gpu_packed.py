@@ -152,3 +152,18 @@ def test_packed_sequence_with_bad_bounds_is_skipped():
     assert bool((run.state_out[1] == 7.0).all())
     assert bool((run.conv_state_out[1] == 7).all())
     _check_against_oracle(run, tok, state, conv_state, cu, Hk, Hv, True, True, "bad bounds", skip=(1,))
+
+
+def test_packed_from_zero_states():
+    """No initial states (NULL state_in and conv_state_in): every sequence starts from zeros."""
+    R = _R()
+    lengths, Hk, Hv = [5, 130, 64], 1, 2
+    tok, _, _, cu, T = _batch(lengths, Hk, Hv, True, True, tag=1340)
+    zeros = np.zeros((len(lengths), Hv, D, D), dtype=np.float32)
+    zcs = np.zeros((len(lengths), 3, 2 * Hk * D + Hv * D), dtype=np.uint16)
+    run = R.PackedPrefill(tok, cu, T, Hk, Hv, True, True, state_in=None, conv_state_in=None)
+    run.run()
+    torch.cuda.synchronize()
+    assert run.exchange_error_word() == 0
+    _check_against_oracle(run, tok, zeros, zcs, cu, Hk, Hv, True, True, "zero states")
+

@@ -114,3 +114,27 @@ def test_long_memory_stress(nseg):
     inp["g"] = np.full((B, T, Hv), -np.log(2.0) / 200000.0, dtype=np.float32)
     print(f"[segments] long memory T={T} segments={nseg}", flush=True)
     _run_and_check(R, inp, B, T, Hk, Hv, True, True, nseg, f"long memory, segments={nseg}")
+
+
+def test_segments_with_gate_logits():
+    """The gate logits are turned into g and beta by the prep kernel, which both paths share."""
+    R = _R()
+    B, T, Hk, Hv = 1, 777, 1, 3
+    w = GI.Workload("seg_gl", B, T, Hk, Hv, random_state=True, random_conv_state=True, tag=1540)
+    inp = GI.make_inputs(w)
+    gl = GI.make_gate_logits(w)
+    g, beta = O.gate_logits(gl["a"], gl["b"], gl["A_log"], gl["dt_bias"])
+    with segments(4):
+        run = R.Prefill(inp, B, T, Hk, Hv, True, True)
+        run.run_gate_logits(gl)
+        torch.cuda.synchronize()
+    assert run.exchange_error_word() == 0
+    ref_inp = dict(inp, g=g.astype(np.float32), beta=beta.astype(np.float32))
+    y_ref, S_ref, cs_ref = O.prefill(ref_inp, B, T, Hk, Hv, True, True)
+    o = R.bits(run.o).reshape(B, T, Hv, D)
+    y = np.stack([bf16_to_f64(o[c // Hv, :, c % Hv]) for c in range(B * Hv)])
+    eo, es = out_errors(y, y_ref), state_error(run.state_out.cpu().numpy().reshape(-1, D, D), S_ref)
+    print(f"[segments] gate logits, 4 segments: e_out={eo['e_out']:.3e} e_state={es:.3e}", flush=True)
+    assert eo["e_out"] <= OUT_TOL and es <= STATE_TOL
+    np.testing.assert_array_equal(R.bits(run.conv_state_out), cs_ref)
+
