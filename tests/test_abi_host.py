@@ -274,3 +274,30 @@ def test_one_hip_runtime_per_process():
             "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
     out = subprocess.run(["python", "-c", code], capture_output=True, text=True, cwd=ROOT, check=True).stdout
     assert out.strip() == "1"
+
+
+def test_two_level_plan_sizes_the_workspace(monkeypatch):
+    """Few heads and a long sequence: the plan splits the sequence into segments, and the
+    workspace grows by their read-outs (32 KB per chunk and head) and segment maps.  The
+    benchmark shapes (16 or more heads) and packed batches keep the plain sequential pass."""
+    few = _shape(B=1, T=262144, Hk=1, Hv=3)
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
+    plain = gdn.gdn_prefill_workspace_size(few)
+    monkeypatch.delenv("GDN_PREFILL_SEGMENTS")
+    planned = gdn.gdn_prefill_workspace_size(few)
+    assert planned - plain >= (262144 // 64) * 3 * 32 * 1024
+    for s in (_shape(B=1, T=4096, Hk=16, Hv=16), _shape(B=4, T=16384, Hk=16, Hv=32),
+              _shape(B=3, T=65536, Hk=1, Hv=3, packed=True)):
+        monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
+        a = gdn.gdn_prefill_workspace_size(s)
+        monkeypatch.delenv("GDN_PREFILL_SEGMENTS")
+        assert gdn.gdn_prefill_workspace_size(s) == a
+    # a forced split asks for more only when the sequence has more than one chunk
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
+    short_plain = gdn.gdn_prefill_workspace_size(_shape(B=1, T=1000, Hk=1, Hv=3))
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "4")
+    assert gdn.gdn_prefill_workspace_size(_shape(B=1, T=1000, Hk=1, Hv=3)) > short_plain
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
+    one_chunk = gdn.gdn_prefill_workspace_size(_shape(B=1, T=64, Hk=1, Hv=3))
+    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "4")
+    assert gdn.gdn_prefill_workspace_size(_shape(B=1, T=64, Hk=1, Hv=3)) == one_chunk
