@@ -1170,54 +1170,77 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // multiple of 64, hence of NCG), so its conv taps and norm weights live in registers
             // once the prologue has staged them.
             const int cgl = vtid % NCG;
-            float hw[32], nw[8];
-            // conv + SiLU of v for chunk cc (raw slot cc % 3, the three rows before it from
-            // sHalo[cc & 1]) -> sV[cc & 1]; the chunk's last three rows -> sHalo[(cc + 1) & 1]
+            float nw[8];
+            // conv + SiLU of v for chunk cc (its raw rows from the ring, the three rows before it
+            // from sHalo[cc & 1]) -> sV[cc & 1]; the chunk's last three raw rows -> sHalo[(cc + 1) & 1].
+            // Conv lane ci owns RPI consecutive rows of 4 channels: it reads each raw row it needs
+            // once (RPI + 3 rows of 8 bytes) and writes each channel's RPI outputs as one packed
+            // store, RPI = 2 with one tile and 4 with two, so that every conv lane has one item.
+            constexpr int RPI = NT == 1 ? 2 : 4;
+            constexpr int NC4 = BV / 4;
+            static_assert((kC / RPI) * NC4 == kConvLanes, "one conv item per conv lane");
+            const int ci = vtid - kConvBase;                          // conv lane, when >= 0
+            const int c4 = (ci > 0 ? ci : 0) % NC4, rg = (ci > 0 ? ci : 0) / NC4;
+            float hwc[16];  // conv taps of the lane's 4 channels: tap j of channel e at 4 e + j
             auto conv_v = [&](int cc) __attribute__((always_inline)) {
-                if (vtid < kConvBase) return;  // not a converting helper
-                _Float16 *dst = sV + (cc & 1) * BV * P64 + cgl * 8 * P64;
-                const uint16_t *cur = sRawV + modn<L::NSLOT>(cc) * kC * BV + cgl * 8;
-                const uint16_t *prev = sHalo + (cc & 1) * 3 * BV + cgl * 8 - (kC - 3) * BV;  // row kC+r2 -> halo row 3+r2
-                if (vtid - kConvBase >= 0 && vtid - kConvBase < 3 * NCG) {
-                    const int r3 = (vtid - kConvBase) / NCG, cg = vtid % NCG;
+                if (ci < 0) return;  // not a converting helper
+                const uint16_t *raw = sRawV + modn<L::NSLOT>(cc) * kC * BV;
+                if (ci < 3 * NCG) {
+                    const int r3 = ci / NCG, cg = ci % NCG;
                     *reinterpret_cast<uint4 *>(sHalo + ((cc + 1) & 1) * 3 * BV + r3 * BV + cg * 8) =
-                        *reinterpret_cast<const uint4 *>(sRawV + modn<L::NSLOT>(cc) * kC * BV + (kC - 3 + r3) * BV + cg * 8);
+                        *reinterpret_cast<const uint4 *>(raw + (kC - 3 + r3) * BV + cg * 8);
                 }
-#pragma unroll 1
-                for (int it = vtid - kConvBase; it < kC * NCG; it += kConvLanes) {
-                    const int row = it / NCG;
-                    uint4 rw[4];
+                const int r0 = rg * RPI;
+                uint2 rw[RPI + 3];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r2 = row - 3 + j;
-                        rw[j] = *reinterpret_cast<const uint4 *>(r2 >= 0 ? cur + r2 * BV : prev + (kC + r2) * BV);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    float x[4][8];
+                for (int j = 0; j < RPI + 3; ++j) {
+                    const int r2 = r0 - 3 + j;  // rows before the chunk come from the halo
+                    rw[j] = *reinterpret_cast<const uint2 *>(
+                        r2 >= 0 ? raw + r2 * BV + c4 * 4 : sHalo + (cc & 1) * 3 * BV + (3 + r2) * BV + c4 * 4);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                float x[RPI + 3][4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) unpack_bf16x8(rw[j], x[j]);
-                    float u8[8];
+                for (int j = 0; j < RPI + 3; ++j) {
+                    x[j][0] = __uint_as_float(rw[j].x << 16);
+                    x[j][1] = __uint_as_float(rw[j].x & 0xffff0000u);
+                    x[j][2] = __uint_as_float(rw[j].y << 16);
+                    x[j][3] = __uint_as_float(rw[j].y & 0xffff0000u);
+                }
+                float u[RPI][4];
+#pragma unroll
+                for (int i = 0; i < RPI; ++i) {
                     if (mcol) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) u8[e] = 0.0f;
+                        for (int e = 0; e < 4; ++e) u[i][e] = 0.0f;
                     } else if (a.conv) {
-                        float acc[8], t8[8];
+                        float acc[4], t4[4];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            acc[e] = hw[4 * e] * x[0][e] + hw[4 * e + 1] * x[1][e] + hw[4 * e + 2] * x[2][e] +
-                                     hw[4 * e + 3] * x[3][e];
+                        for (int e = 0; e < 4; ++e)
+                            acc[e] = hwc[4 * e] * x[i][e] + hwc[4 * e + 1] * x[i + 1][e] + hwc[4 * e + 2] * x[i + 2][e] +
+                                     hwc[4 * e + 3] * x[i + 3][e];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) t8[e] = __builtin_amdgcn_exp2f(acc[e] * -1.4426950408889634f);
+                        for (int e = 0; e < 4; ++e) t4[e] = __builtin_amdgcn_exp2f(acc[e] * -1.4426950408889634f);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) t8[e] = __builtin_amdgcn_rcpf(1.0f + t8[e]);
+                        for (int e = 0; e < 4; ++e) t4[e] = __builtin_amdgcn_rcpf(1.0f + t4[e]);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) u8[e] = acc[e] * t8[e];
+                        for (int e = 0; e < 4; ++e) u[i][e] = acc[e] * t4[e];
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) u8[e] = x[3][e];
+                        for (int e = 0; e < 4; ++e) u[i][e] = x[i + 3][e];
                     }
+                }
+                _Float16 *dst = sV + (cc & 1) * BV * P64 + c4 * 4 * P64 + r0;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) dst[e * P64 + row] = static_cast<_Float16>(u8[e]);
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (RPI == 2) {
+                        *reinterpret_cast<halfx2 *>(dst + e * P64) =
+                            halfx2{static_cast<_Float16>(u[0][e]), static_cast<_Float16>(u[1][e])};
+                    } else {
+                        *reinterpret_cast<half4 *>(dst + e * P64) =
+                            half4{static_cast<_Float16>(u[0][e]), static_cast<_Float16>(u[1][e]),
+                                  static_cast<_Float16>(u[2][e]), static_cast<_Float16>(u[3][e])};
+                    }
                 }
             };
             // gated RMSNorm + store of chunk oc
@@ -1270,7 +1293,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             unsigned long long *mrow = a.mbox + (size_t)chain * kTiles * kRing * kC + lane;  // row = lane
             lds_barrier();
 #pragma unroll
-            for (int e = 0; e < 32; ++e) hw[e] = sCW[cgl * 32 + e];
+            for (int e = 0; e < 16; ++e) hwc[e] = sCW[c4 * 16 + e];
 #pragma unroll
             for (int e = 0; e < 8; ++e) nw[e] = sNW[cgl * 8 + e];
             conv_v(0);
