@@ -63,6 +63,13 @@ constexpr int kMaxTokens = kMaxDecodeTokens;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf(const void *p, unsigned int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
 }
+// Cache policy of the state traffic, which every call streams once: loads marked
+// non-temporal (nt) and stores written through at agent scope (sc1).  Measured on a
+// read-modify-write of 805 MB in 64 KiB pieces, the decode's pattern: 6.05 TB/s
+// against 5.45 TB/s with the default policy.  Only the caching changes; the kernel
+// boundary orders the stores for whatever reads the state next.
+constexpr int kStateLoadPolicy = 2;    // nt
+constexpr int kStateStorePolicy = 16;  // sc1
 
 // LDS of one workgroup, in floats, for T tokens and r value heads per key head.
 struct DecodeLds {
@@ -217,8 +224,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAXT <
         const int vo = dummy ? 0 : toff;
 #pragma unroll
         for (int m = 0; m < kRows; ++m)
-            S[m] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rstate, vo,
-                                                                                     hr * kHeadBytes + m * 16 * kD * 4, 0));
+            S[m] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rstate, vo, hr * kHeadBytes + m * 16 * kD * 4, kStateLoadPolicy));
     };
 
     // ---- 0. every small input first: the conv item's raw rows and weights, z, the gates
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAXT <
                 S[m] = sv;
                 if (keep)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sv), rdst, toff,
-                                                           hr * kHeadBytes + m * 16 * kD * 4, 0);
+                                                           hr * kHeadBytes + m * 16 * kD * 4, kStateStorePolicy);
             }
             // The stores' data registers stay untouched until all eight are issued: after the
             // last token the state is otherwise dead, and the compiler would reuse one register
