@@ -903,11 +903,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NSL = (SEG ? 2 : 1) * kTiles / NT;
     constexpr int NCG = BV / 8;                 // 8-column groups per slice row
     constexpr int NV = 8 - 2 * NT - 1;          // VALU helper waves
-    // Helper 0 runs the norm's exchange; helpers 1 and 2 gate; conv(v) runs on the rest
-    // (NT = 1: helpers 3, 4) or, with only three helpers (NT = 2), on helpers 1 and 2.
+    // Helper 0 runs the norm's exchange; helpers 1 and 2 gate.  With five helpers (NT = 1)
+    // conv(v) runs on helpers 3 and 4.  With three (NT = 2) the transcendental work is
+    // spread evenly instead: the conv of rows 0..31 goes to helper 0 (the conv touches LDS
+    // only, so it does not make the exchange's loads wait), rows 32..63 to helper 1, and
+    // the gating's 256 row pieces to helper 1 (64) and helper 2 (192): 48 exponentials and
+    // reciprocals per lane on helpers 1 and 2 and 32 on helper 0, against 64 on helpers 1
+    // and 2 with the conv split between them alone.
     constexpr int kGateLanes = 128;                       // helpers 1, 2
-    constexpr int kConvBase = NT == 1 ? 192 : 64;         // first helper lane that converts v
-    constexpr int kConvLanes = NV * 64 - kConvBase;
+    constexpr int kConvBase = NT == 1 ? 192 : 0;          // first helper lane that converts v
+    constexpr int kConvLanes = 128;
     static_assert(NV >= 3 && (NT == 2 || NV == 5), "helper roles");
     constexpr int NRD = kC * BV * 2 / 1024;     // DMA instructions for 64 rows of raw v (or z) of the slice
     constexpr int GROUP = kOpSlot / 1024 + 2 * NRD;  // DMA instructions the load wave issues per iteration
@@ -1179,7 +1184,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             constexpr int RPI = NT == 1 ? 2 : 4;
             constexpr int NC4 = BV / 4;
             static_assert((kC / RPI) * NC4 == kConvLanes, "one conv item per conv lane");
-            const int ci = vtid - kConvBase;                          // conv lane, when >= 0
+            const int ci = vtid >= kConvBase && vtid < kConvBase + kConvLanes ? vtid - kConvBase : -1;  // conv lane
             const int c4 = (ci > 0 ? ci : 0) % NC4, rg = (ci > 0 ? ci : 0) / NC4;
             float hwc[16];  // conv taps of the lane's 4 channels: tap j of channel e at 4 e + j
             auto conv_v = [&](int cc) __attribute__((always_inline)) {
@@ -1248,8 +1253,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const float *src = sO + (oc % kORing) * VT + cgl * 8 * PL;
                 const float *rs = sRstd + (oc & 1) * kC;
                 const uint16_t *zt = sZ + modn<L::NSLOT>(oc) * kC * BV + cgl * 8;
+                // NT = 1: one row piece per gating lane; NT = 2: helper 1 one, helper 2 three
+                const int gstep = NT == 1 ? kGateLanes : (vh == 1 ? kC * NCG : 64);
 #pragma unroll 1
-                for (int it = vtid - 64; it < kC * NCG; it += kGateLanes) {
+                for (int it = vtid - 64; it < kC * NCG; it += gstep) {
                     const int row = it / NCG;
                     const int tt = oc * kC + row;
                     float y[8];
@@ -1315,6 +1322,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 };
                 mb_request(-2 - kLag);
                 for (int c = 0; c <= last; ++c) {
+                    if (NT == 2 && c + 1 < nch) conv_v(c + 1);  // rows 0..31 of the conv
                     // 1/rms of chunk rc from the siblings' words (published kLag - 1 iterations before
                     // they were requested; a word without the chunk's tag is waited for)
                     const int rc = c - 2 - kLag;
@@ -1349,7 +1357,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             } else {
                 for (int c = 0; c <= last; ++c) {
-                    if (vtid >= kConvBase && c + 1 < nch) conv_v(c + 1);
+                    if (c + 1 < nch) conv_v(c + 1);  // nothing for a lane without a conv item
                     const int oc = c - 3 - kLag;
                     if (vtid < 64 + kGateLanes && oc >= 0 && oc < nch) gate(oc);
                     lds_barrier();
