@@ -183,3 +183,22 @@ def test_multi_full_27b_decode_shape():
     m.run()
     torch.cuda.synchronize()
     _against_oracle(R, m, inp, B, T, Hk, Hv, True, True, "27B-shaped B=256 T=2")
+
+
+@pytest.mark.parametrize("B,T,Hk,Hv", [
+    (2, 1, 1, 64),  # 64 value heads per key head: 1,056 conv items and 1,024 z pieces for 512 threads
+    (2, 8, 1, 8),   # 8 tokens of 8 value heads: about 75 KB of LDS, above the default dynamic limit
+    (1, 3, 2, 64),  # 32 per key head with 3 tokens: both of the above at once (about 89 KB)
+])
+def test_decode_many_value_heads_per_key_head(B, T, Hk, Hv):
+    """Head ratios and token counts past one item per thread and past 64 KB of LDS: the
+    second passes over conv items and z pieces and the raised LDS limit, against the oracle."""
+    R = _R()
+    w = GI.Workload(f"multi_wide_{B}_{T}_{Hk}_{Hv}", B, T, Hk, Hv, random_state=True, random_conv_state=True,
+                    tag=1450 + T + Hv)
+    inp = GI.make_inputs(w)
+    print(f"[decode multi] wide B={B} T={T} {Hk}/{Hv}", flush=True)
+    m = Multi(R, inp, B, T, Hk, Hv, True, True)
+    m.run()
+    torch.cuda.synchronize()
+    _against_oracle(R, m, inp, B, T, Hk, Hv, True, True, f"{Hk}/{Hv} T={T}")
