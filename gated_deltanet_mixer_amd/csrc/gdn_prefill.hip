@@ -500,9 +500,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         // diagonal 16x16 blocks of T = (I + L)^{-1}: forward substitution, one column per lane,
         // column-oriented (once x[mm] is final it is subtracted from every later row at once),
         // so the dependent steps are the 15 rows rather than every product; the products and
-        // their order per row are those of the row-by-row form
-        if (lane < 16) {
-            const int w0 = 16 * wave, cidx = lane;
+        // their order per row are those of the row-by-row form.  One wave takes all four
+        // blocks (block lane / 16, column lane % 16): the same dependent steps with every lane
+        // busy, where one block per wave left three quarters of four waves' issue slots idle
+        // (this kernel is bound by VALU issue)
+        if (wave == (hr & 3)) {
+            const int blk = lane >> 4, w0 = 16 * blk, cidx = lane & 15;
             float x[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) x[rr] = rr == cidx ? 1.0f : 0.0f;
@@ -513,10 +516,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 for (int rr = mm + 1; rr < 16; ++rr) x[rr] -= sL[(w0 + rr) * PL + w0 + mm] * xm;
             }
             const float bc = sB[w0 + cidx];
-            const int db = wave * (wave + 1) / 2 + wave;
+            const int db = blk * (blk + 1) / 2 + blk;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                sTd[(wave * 16 + rr) * PTD + cidx] = x[rr];
+                sTd[(blk * 16 + rr) * PTD + cidx] = x[rr];
                 sT16T[(w0 + cidx) * P64 + w0 + rr] = static_cast<_Float16>(x[rr]);
                 sTbst[db * kBlk + rr * 16 + cidx] = static_cast<_Float16>(x[rr] * bc);
             }
