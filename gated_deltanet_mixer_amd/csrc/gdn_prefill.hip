@@ -211,6 +211,12 @@ __device__ __forceinline__ int find_seq(const int *cu, int B, int gc, int lane) 
     return lo;
 }
 
+// e^x from the hardware base-2 exponential (v_exp_f32, about 1 ulp): the prep kernel is bound
+// by VALU issue, and the library exp's range handling costs several instructions per call.
+// Its arguments are log-decay sums (never positive past rounding); results that would be
+// denormal flush to zero, which the decays they stand for are to fp16 precision anyway.
+__device__ __forceinline__ float hw_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 struct PrepArgs {
     const uint16_t *q, *k, *conv_w, *conv_state_in;
     const float *g, *beta;      // or the gate logits a, b when A_log is set
@@ -377,7 +383,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 for (int e = 0; e < 8; ++e) ss += uu[i][e] * uu[i][e];
                 ss = group_sum<16>(ss);
                 const bool valid = tc0 + tl0 + i < si.T;
-                const float sc = valid ? qscale / sqrtf(ss + a.eps_l2) : 0.0f;  // rows past T are zero
+                // rows past T are zero; the hardware reciprocal square root (about 1 ulp) is far
+                // inside the fp16 the result is stored in
+                const float sc = valid ? qscale * __builtin_amdgcn_rsqf(ss + a.eps_l2) : 0.0f;
                 half8 hv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) hv[e] = static_cast<_Float16>(uu[i][e] * sc);
@@ -468,9 +476,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const float gc = __shfl(gv, 63, 64);
             sG[lane] = gv;
             sB[lane] = bv;
-            st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * lane, __expf(gv));
-            st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * (kC + lane), __expf(gc - gv));
-            if (lane < 4) st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * (2 * kC + lane), __expf(gc));
+            st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * lane, hw_exp(gv));
+            st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * (kC + lane), hw_exp(gc - gv));
+            if (lane < 4) st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * (2 * kC + lane), hw_exp(gc));
         }
         lds_barrier();
 
@@ -487,7 +495,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * ti + 4 * lq + e;
-                const float rdec = __expf(sG[row] - gcol);
+                const float rdec = hw_exp(sG[row] - gcol);
                 if (isP)
                     sPst[tt * kBlk + (4 * lq + e) * 16 + l16] =
                         static_cast<_Float16>(col <= row ? raw[u][e] * rdec : 0.0f);
