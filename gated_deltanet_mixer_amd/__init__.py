@@ -20,6 +20,8 @@ GDN_EINVAL = -1
 GDN_EUNSUPPORTED = -2
 GDN_EHIP = -3
 GDN_EWORKSPACE = -4
+GDN_ETIMEOUT = -5
+GDN_ESKIPPED = -6
 GDN_NO_NORM = 1
 GDN_PACKED = 2
 
@@ -36,15 +38,17 @@ class GdnError(RuntimeError):
 class gdn_shape(C.Structure):
     _fields_ = [("B", C.c_int32), ("T", C.c_int32), ("Hk", C.c_int32), ("Hv", C.c_int32),
                 ("Dk", C.c_int32), ("Dv", C.c_int32), ("conv_width", C.c_int32), ("flags", C.c_uint32),
-                ("eps_l2", C.c_float), ("eps_norm", C.c_float)]
+                ("eps_l2", C.c_float), ("eps_norm", C.c_float), ("prefill_segments", C.c_int32)]
 
 
 def make_shape(B: int, T: int, Hk: int, Hv: int, conv: bool = True, norm: bool = True,
                eps_l2: float = 1e-6, eps_norm: float = 1e-6, Dk: int = 128, Dv: int = 128,
-               packed: bool = False) -> gdn_shape:
-    """packed: B sequences of T tokens in all (gdn_prefill_packed)."""
+               packed: bool = False, segments: int = 0) -> gdn_shape:
+    """packed: B sequences of T tokens in all (gdn_prefill_packed).  segments: 0 lets the
+    library choose between the plain sequential pass and the two-level scan, 1 forces the
+    plain pass, n >= 2 asks for n segments."""
     flags = (0 if norm else GDN_NO_NORM) | (GDN_PACKED if packed else 0)
-    return gdn_shape(B, T, Hk, Hv, Dk, Dv, 4 if conv else 0, flags, eps_l2, eps_norm)
+    return gdn_shape(B, T, Hk, Hv, Dk, Dv, 4 if conv else 0, flags, eps_l2, eps_norm, segments)
 
 
 # torch ships its own copy of the HIP runtime under the same soname.  Loading
@@ -74,11 +78,12 @@ _lib.gdn_prefill_packed.argtypes = [_sp] + [_vp] * 15 + [C.c_size_t, _vp]
 _lib.gdn_decode_multi.argtypes = [_sp] + [_vp] * 14
 _lib.gdn_decode_multi_gate_logits.argtypes = [_sp] + [_vp] * 16
 _lib.gdn_prefill_packed_gate_logits.argtypes = [_sp] + [_vp] * 17 + [C.c_size_t, _vp]
+_lib.gdn_prefill_check.argtypes = [_vp, C.c_size_t, _vp]
 
 EXPORTED = ("gdn_state_init", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
             "gdn_prefill_gate_logits", "gdn_decode_step_gate_logits", "gdn_prefill_packed",
             "gdn_prefill_packed_gate_logits", "gdn_decode_multi", "gdn_decode_multi_gate_logits",
-            "gdn_status_string", "gdn_last_error")
+            "gdn_prefill_check", "gdn_status_string", "gdn_last_error")
 
 
 def _ptr(t):
@@ -129,6 +134,14 @@ def gdn_prefill(shape: gdn_shape, q, k, v, g, beta, z, conv_w, norm_w, state_in,
                           _ptr(state_out), _ptr(conv_state_out), _ptr(workspace), int(workspace_bytes),
                           _stream(stream))
     _check("gdn_prefill", rc)
+
+
+def gdn_prefill_check(workspace, workspace_bytes: int | None = None, stream=None) -> None:
+    """Wait for the stream and raise GdnError if the last prefill on this workspace left
+    an error bit (a timed-out wait between workgroups, or a skipped packed sequence)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("gdn_prefill_check", _lib.gdn_prefill_check(_ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def gdn_decode_step(shape: gdn_shape, q, k, v, g, beta, z, conv_w, norm_w, state, conv_state, o,

@@ -36,6 +36,7 @@ int check_shape(const gdn_shape *s, bool use_T) {
     if (s->conv_width != 0 && s->conv_width != 4) return GDN_EUNSUPPORTED;
     if (s->flags & ~(GDN_NO_NORM | GDN_PACKED)) return GDN_EINVAL;
     if (!(s->eps_l2 >= 0.0f) || !(s->eps_norm >= 0.0f)) return GDN_EINVAL;
+    if (s->prefill_segments < 0 || ((s->flags & GDN_PACKED) && s->prefill_segments > 1)) return GDN_EINVAL;
     // sizes must fit the kernels' 32-bit token and head indices
     if ((long long)s->B * s->Hv * kD > 0x7fffffffLL || (use_T && (long long)s->T * kD > 0x7fffffffLL))
         return GDN_EINVAL;
@@ -58,6 +59,8 @@ const char *gdn_status_string(int status) {
     case GDN_EUNSUPPORTED: return "unsupported shape (head width must be 128, conv width 0 or 4)";
     case GDN_EHIP: return "a HIP call or kernel launch failed";
     case GDN_EWORKSPACE: return "workspace too small";
+    case GDN_ETIMEOUT: return "a bounded wait between workgroups timed out: the prefill outputs are wrong";
+    case GDN_ESKIPPED: return "a packed sequence with invalid bounds was skipped";
     default: return "unknown status";
     }
 }
@@ -78,9 +81,22 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes) {
     if (rc) return rc;
     if (!bytes) return GDN_EINVAL;
     PrefillPlan plan;
-    plan_prefill(shape->B, shape->T, shape->Hk, shape->Hv, (shape->flags & GDN_PACKED) != 0, &plan);
+    plan_prefill(shape->B, shape->T, shape->Hk, shape->Hv, (shape->flags & GDN_PACKED) != 0, shape->prefill_segments,
+                 &plan);
     if (plan.nslots * shape->Hk > 0x7fffffffLL) return GDN_EINVAL;
     *bytes = plan.total_bytes;
+    return GDN_OK;
+}
+
+int gdn_prefill_check(const void *workspace, size_t workspace_bytes, void *stream) {
+    if (!workspace || workspace_bytes < kHeaderBytes || !aligned(workspace, 16)) return GDN_EINVAL;
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail("hipStreamSynchronize", e), GDN_EHIP;
+    unsigned int word = 0;
+    e = hipMemcpy(&word, static_cast<const unsigned char *>(workspace) + kErrOffset, sizeof word, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail("hipMemcpy(error word)", e), GDN_EHIP;
+    if (word & 1u) return GDN_ETIMEOUT;
+    if (word & 2u) return GDN_ESKIPPED;
     return GDN_OK;
 }
 
@@ -137,7 +153,7 @@ int prefill_impl(const gdn_shape *s, const int32_t *cu_seqlens, const uint16_t *
         return GDN_EINVAL;
 
     PrefillPlan plan;
-    plan_prefill(s->B, s->T, s->Hk, s->Hv, packed, &plan);
+    plan_prefill(s->B, s->T, s->Hk, s->Hv, packed, s->prefill_segments, &plan);
     if (plan.nslots * s->Hk > 0x7fffffffLL) return GDN_EINVAL;
     if (workspace_bytes < plan.total_bytes) return GDN_EWORKSPACE;
 

@@ -32,31 +32,52 @@ struct PrefillParams {
 };
 
 // Value-dimension slicing and workspace layout chosen for a prefill shape.
+// The workspace starts with the exchange area (its first 32-bit word is the error word),
+// which the prep kernel clears at the start of every call; the operand blocks follow.
 struct PrefillPlan {
-    int nt;              // 16-column value tiles per chain workgroup: 1 or 2
-    int bv;              // value columns per chain workgroup (16 * nt)
+    int nt;              // 16-column value tiles per sequential-pass workgroup: 1 or 2
+    int bv;              // value columns per sequential-pass workgroup (16 * nt)
     int nslice;          // workgroups per (sequence, value head): 128 / bv
     int nchunks;         // ceil(T / 64)
     long long nslots;    // chunk operand slots: B nchunks, or floor(T / 64) + B for packed sequences
-    size_t qk_bytes;     // per (slot, key head): q^, k^ [64][128], k^T [128][64] fp16
+    size_t xch_bytes;    // exchange area: 256-byte header (error word, queue tickets, exit count),
+                         // tagged per-row partial sums of every (sequence, value head), counters
+    size_t mbox_bytes;   // the tagged partial sums inside the exchange area
+    size_t qk_bytes;     // per (slot, key head): q^, k^, k^T fragments (fp16)
     size_t tp_bytes;     // per (slot, value head): T diag(beta), P (lower blocks, fp16), decay vectors
-    size_t ready_bytes;  // per (slot, key head): stamp of the call whose operands are written
-    size_t mbox_bytes;   // exchange area (tagged partial sums, counters, error word)
     int nseg;            // segments per sequence of the two-level scan (1: the plain sequential pass)
     int seg_chunks;      // chunks per segment
     size_t seg_out_bytes, seg_state_bytes, seg_frag_bytes;  // two-level scan: read-outs, segment maps, start states
     size_t total_bytes;
 };
 
+// Where each region of a prefill workspace lies.
+struct PrefillRegions {
+    unsigned int *err;       // error word: bit 0 a bounded wait timed out, bit 1 a packed sequence was skipped
+    unsigned int *tickets;   // [8] work-queue tickets
+    unsigned int *exits;     // workgroups that left the two-level scan's first pass
+    unsigned long long *mbox;
+    unsigned int *counters;  // [B Hv]
+    _Float16 *qkf, *tpf;
+    unsigned char *seg;      // two-level scan regions (read-outs, segment maps, start states)
+};
+
+// Byte offsets inside the header of the exchange area.
+constexpr size_t kErrOffset = 0, kTicketOffset = 64, kExitOffset = 128, kHeaderBytes = 256;
+
 // Record why a launch failed, for gdn_last_error() on the calling thread;
 // both return -1 so a launcher can `return fail(...)`.
 int fail(const char *what, hipError_t e);
 int fail(const char *what);
 
-int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan);
+// segments: 0 lets the plan choose, 1 keeps the plain sequential pass, n >= 2 asks for n
+// segments of the two-level scan (even batches only).
+int plan_prefill(int B, int T, int Hk, int Hv, bool packed, int segments, PrefillPlan *plan);
+PrefillRegions prefill_regions(void *workspace, const PrefillPlan &plan, int B, int Hv);
 int launch_decode(const DecodeParams &p, hipStream_t stream);
 size_t decode_lds_bytes(int T, int r);  // LDS of one decode workgroup
 int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream);
+int launch_pass(const PrefillParams &p, const PrefillPlan &plan, const PrefillRegions &rg, hipStream_t stream);
 int launch_state_init(float *state, size_t n_state, uint16_t *conv_state, size_t n_conv,
                       hipStream_t stream);
 

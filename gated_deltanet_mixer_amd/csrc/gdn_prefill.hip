@@ -56,166 +56,13 @@
 #include <cstdlib>
 #include <mutex>
 
-#include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_prefill_common.h"
 
 namespace gdn {
 
 namespace {
 
-constexpr int kD = 128;        // head width
-constexpr int kC = 64;         // chunk length
-constexpr int kTiles = 8;      // 16-column tiles per head
-constexpr uint32_t kSpinLimit = 1u << 20;  // bound of every cross-workgroup wait (~0.3 s)
-
-// LDS pitches (elements) so that 16-row MFMA fragment reads hit distinct banks.
-constexpr int P128 = kD + 8;   // fp16 rows of 128
-constexpr int P64 = kC + 8;    // fp16 rows of 64
-constexpr int PL = kC + 4;     // fp32 rows of 64
-constexpr int PTD = 20;        // fp32 rows of a 16x16 block
-
-// Workspace blocks (fp16 elements), written by the prep kernel as MFMA operand
-// fragments: fragment f holds, for lane L = l16 + 16 lq, the 8 values of row
-// (tile row) + l16 at contraction indices 32 ks + {4 lq .. 4 lq + 3} and
-// 32 ks + 16 + {4 lq .. 4 lq + 3} -- the rows of two adjacent 16-row
-// accumulator tiles as they sit in one lane.
-//   per (sequence, chunk, key head), kQKF:  q^ f = 0..15 and k^ f = 16..31 (row tile f>>2,
-//                                           k-step f&3 over keys)
-//   per (sequence, chunk, value head), kTPF: T diag(beta) f = 0..5 (lower-triangular 64x64,
-//                                           only the blocks that are not all zero), fp32
-//                                           e^{G_i} [64], e^{G_C - G_i} [64], e^{G_C} [4]
-//                                           (1 KB), then P = (Q K^T) o R f = 0..5
-// k^T is never stored: the sequential pass reads it from the k^ fragments in
-// LDS with the transposing LDS read.
-constexpr int kBlk = 256;                              // one 16x16 block (prep staging)
-constexpr int kFrag = 64 * 8;                          // one fragment: 64 lanes x 8 fp16
-constexpr int kQKF = 32 * kFrag;
-constexpr int kKOff = 16 * kFrag;                      // k^ fragments inside a q/k block
-constexpr int kVecOff = 6 * kFrag;
-constexpr int kPOff = kVecOff + 512;                   // after 256 fp32
-constexpr int kTPF = kPOff + 6 * kFrag;
-
-__host__ __device__ constexpr int kpos(int m) { return m < 4 ? 8 * m : 8 * (m - 4) + 4; }
-
-__device__ __forceinline__ void tri_block(int blk, int &bi, int &bj) {
-    bi = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
-    bj = blk - bi * (bi + 1) / 2;
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
-// Accumulator tiles a (rows 4q..4q+3 of a 16-row tile) and b (the next tile)
-// as one 8-element MFMA B operand, in the permuted k order described above.
-__device__ __forceinline__ half8 pack_tiles(const floatx4 &a, const floatx4 &b) {
-    return half8{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3],
-                 (_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
-}
-
-#define GDN_AS1 __attribute__((address_space(1)))
-#define GDN_AS3 __attribute__((address_space(3)))
-
-// 16 bytes per lane from global memory (lane address) into LDS at dst + 16 lane
-__device__ __forceinline__ void dma16(const void *src_lane, void *dst_wave) {
-    __builtin_amdgcn_global_load_lds((const GDN_AS1 void *)src_lane, (GDN_AS3 void *)dst_wave, 16, 0, 0);
-}
-// the same through a buffer resource: lanes past the resource read as zero
-__device__ __forceinline__ void dma16b(__amdgpu_buffer_rsrc_t r, int voff, void *dst_wave) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (GDN_AS3 void *)dst_wave, 16, voff, 0, 0, 0);
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, unsigned int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ half8 ld_frag(__amdgpu_buffer_rsrc_t r, int voff, int f) {
-    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, f * 1024, 0));
-}
-__device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-    const floatx4 v = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-    return make_float4(v[0], v[1], v[2], v[3]);
-}
-// wait until at most N vector-memory operations of this wave are outstanding
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// Stores of operands that the sequential pass may read while the prep kernel
-// still runs: written through to memory (agent-coherent, the encoding of an
-// agent-scope relaxed atomic store), so a block can publish its stamp after its
-// stores complete without writing back a whole L2.
-// Workspace stores of the prep kernel: written through to memory (sc1) when the sequential
-// pass may read them while the prep kernel still runs, ordinary stores otherwise (the
-// kernel boundary then orders them).
-constexpr int kWriteThrough = 16;  // sc1
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-template <bool THROUGH>
-__device__ __forceinline__ void st_ws(__amdgpu_buffer_rsrc_t r, int voff, half8 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, THROUGH ? kWriteThrough : 0);
-}
-template <bool THROUGH>
-__device__ __forceinline__ void st_ws(__amdgpu_buffer_rsrc_t r, int voff, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, THROUGH ? kWriteThrough : 0);
-}
-
-// 4 fp16 from LDS through the transposing read: within each 16-lane group the
-// lanes' 8-byte chunks form a 4 x 16 matrix (row = lane / 4, column = 4 (lane % 4)
-// + element) and lane i receives column i.
-__device__ __forceinline__ half4 lds_tr16(const _Float16 *p) {
-    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short v4s;
-    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDN_AS3 v4s *)(p));
-    return __builtin_bit_cast(half4, r);
-}
-
-// ========================================================================
-// chunk_prep_kernel
-// ========================================================================
-
-// Where sequence b's tokens and chunk operands sit.  An even batch (cu == nullptr):
-// tokens b T .. b T + T - 1 and operand slots b nch .. b nch + nch - 1.  Packed
-// sequences: tokens cu[b] .. cu[b+1] - 1 and slots from floor(cu[b] / 64) + b on.
-// Those bases grow from one sequence to the next by at least the chunk count of
-// the earlier one, so the slot ranges never overlap and all of them lie below
-// floor(T / 64) + B, without a prefix sum over the chunk counts.  Chunks start at
-// each sequence's first token: the recurrent state and the conv window start
-// afresh at every sequence boundary.  A packed sequence whose bounds are not
-// 0 <= cu[b] < cu[b+1] <= T comes back with no chunks (and nothing is read or
-// written for it).
-struct SeqInfo {
-    size_t tok0;
-    int T, c0, nch;
-};
-__device__ __forceinline__ SeqInfo seq_info(const int *cu, int b, int T, int nch) {
-    if (!cu) return SeqInfo{(size_t)b * T, T, b * nch, nch};
-    const int t0 = cu[b], t1 = cu[b + 1];
-    if (!(0 <= t0 && t0 < t1 && t1 <= T)) return SeqInfo{0, 0, 0, 0};
-    return SeqInfo{(size_t)t0, t1 - t0, t0 / kC + b, (t1 - t0 + kC - 1) / kC};
-}
-
-// Packed sequences: the sequence whose slot range may hold slot gc, the last b
-// in [0, B) with floor(cu[b] / 64) + b <= gc (those bases increase with b).  A
-// 64-way search, one wave: every lane tests one candidate per round, so B <= 64
-// takes one round of loads and B <= 4096 two.  The result is wave-uniform.
-__device__ __forceinline__ int find_seq(const int *cu, int B, int gc, int lane) {
-    int lo = 0, n = B;  // the answer lies in [lo, lo + n)
-    while (n > 1) {
-        const int step = (n + 63) >> 6;
-        const int cand = lo + lane * step;
-        const bool le = lane * step < n && cu[cand] / kC + cand <= gc;
-        const unsigned long long m = __ballot(le);
-        const int j = m ? 63 - __clzll(m) : 0;
-        lo += j * step;
-        n = min(step, n - j * step);
-    }
-    return lo;
-}
-
-// e^x from the hardware base-2 exponential (v_exp_f32, about 1 ulp): the prep kernel is bound
-// by VALU issue, and the library exp's range handling costs several instructions per call.
-// Its arguments are log-decay sums (never positive past rounding); results that would be
-// denormal flush to zero, which the decays they stand for are to fp16 precision anyway.
-__device__ __forceinline__ float hw_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 struct PrepArgs {
     const uint16_t *q, *k, *conv_w, *conv_state_in;
@@ -224,8 +71,8 @@ struct PrepArgs {
     uint16_t *conv_state_out;
     _Float16 *qkf;  // [B][nch][Hk][kQKF]
     _Float16 *tpf;  // [B][nch][Hv][kTPF]
-    unsigned int *ready;  // [chunks][Hk]: call stamp once the block's operands are written
-    unsigned int stamp;
+    uint4 *clear;         // exchange area of the workspace, zeroed at the start of every call
+    size_t clear_n16;     // its size in 16-byte units
     const int *cu;                     // packed sequences: [B + 1] token offsets (nullptr: even batch)
     int B, T, Hk, Hv, r, Cc, conv, nch;  // nch: chunks per sequence of an even batch
     float eps_l2;
@@ -248,9 +95,8 @@ struct PrepLds {
     static size_t bytes(int r) { return sGr + 2 * 4 * (size_t)kC * r; }
 };
 
-// grid (slots * Hk), 256 threads: slot b nch + c of an even batch, else where seq_info places it
-// THROUGH: the sequential pass runs at the same time and follows the ready stamps.
-template <bool THROUGH>
+// grid (slots * Hk), 256 threads: slot b nch + c of an even batch, else where seq_info places it.
+// The sequential pass runs after this kernel on the same stream, so plain stores suffice.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_prep_kernel(PrepArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     _Float16 *sQ = reinterpret_cast<_Float16 *>(smem + PrepLds::sQ);
@@ -270,16 +116,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     // sequence), so the sequential pass can start on the first chunks while later ones are
     // still being prepared
     const int gc = blockIdx.x / a.Hk, kh = blockIdx.x % a.Hk;
+    // the exchange area (error word, queue tickets, mailbox) starts every call at zero
+    for (size_t i = (size_t)blockIdx.x * 256 + tid; i < a.clear_n16; i += (size_t)gridDim.x * 256)
+        a.clear[i] = make_uint4(0, 0, 0, 0);
     const int b = a.cu ? find_seq(a.cu, a.B, gc, lane) : gc / a.nch;
-    const SeqInfo si = seq_info(a.cu, b, a.T, a.nch);
+    const SeqInfo si = seq_info(a.cu, b, a.T, a.nch, a.B);
     const int c = gc - si.c0;
-    if (c < 0 || c >= si.nch) {
-        // a slot between two packed sequences' ranges (or of an invalid one): nothing to
-        // prepare; its stamp is still set, so that no wait on it can outlast this kernel
-        if (tid == 0)
-            __hip_atomic_store(a.ready + (size_t)gc * a.Hk + kh, a.stamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
+    if (c < 0 || c >= si.nch) return;  // a slot between two packed sequences' ranges: nothing to prepare
     const int tc0 = c * kC;
     float *sGr = reinterpret_cast<float *>(smem + PrepLds::sGr);
 
@@ -427,7 +270,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
     lds_barrier();
 
-    // ---- 1b. q^ and k^ to the workspace as operand fragments
+    // ---- 1b. q^, k^ and k^T to the workspace as operand fragments
     {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qkf + ((size_t)gc * a.Hk + kh) * kQKF, kQKF * 2);
         for (int idx = tid; idx < 32 * 64; idx += 256) {
@@ -436,7 +279,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const int ff = f & 15;
             const _Float16 *src = M + (16 * (ff >> 2) + fl) * P128 + 32 * (ff & 3) + 4 * fq;
             const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
-            st_ws<THROUGH>(rq, idx * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            st_ws<false>(rq, idx * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+        // k^T fragment 32 + 2 ti + s2, lane fl + 16 fq: key 16 ti + fl at tokens
+        // 32 s2 + 4 fq + e and 32 s2 + 16 + 4 fq + e (e = 0..3)
+        for (int idx = tid; idx < 16 * 64; idx += 256) {
+            const int ft = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
+            const int ti = ft >> 1, s2 = ft & 1;
+            const _Float16 *src = sK + (32 * s2 + 4 * fq) * P128 + 16 * ti + fl;
+            half8 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = src[e * P128];
+                v[4 + e] = src[(16 + e) * P128];
+            }
+            st_ws<false>(rq, (32 * 64 + idx) * 16, v);
         }
     }
 
@@ -476,9 +333,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const float gc = __shfl(gv, 63, 64);
             sG[lane] = gv;
             sB[lane] = bv;
-            st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * lane, hw_exp(gv));
-            st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * (kC + lane), hw_exp(gc - gv));
-            if (lane < 4) st_ws<THROUGH>(rtp, kVecOff * 2 + 4 * (2 * kC + lane), hw_exp(gc));
+            st_ws<false>(rtp, kVecOff * 2 + 4 * lane, hw_exp(gv));
+            st_ws<false>(rtp, kVecOff * 2 + 4 * (kC + lane), hw_exp(gc - gv));
+            if (lane < 4) st_ws<false>(rtp, kVecOff * 2 + 4 * (2 * kC + lane), hw_exp(gc));
         }
         lds_barrier();
 
@@ -597,19 +454,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }
-            st_ws<THROUGH>(rtp, ((f < 6 ? 0 : kPOff - 6 * kFrag) + idx * 8) * 2, v);
+            st_ws<false>(rtp, ((f < 6 ? 0 : kPOff - 6 * kFrag) + idx * 8) * 2, v);
         }
         lds_barrier();
     }
-    // every wave's (written-through) stores complete, then the block's stamp; with the
-    // sequential pass waiting for this kernel to end, the stamp needs no ordering
-    if (THROUGH) {
-        wait_vmcnt<0>();
-        __syncthreads();
-    }
-    if (tid == 0)
-        __hip_atomic_store(a.ready + (size_t)gc * a.Hk + kh, a.stamp, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ========================================================================
@@ -841,27 +689,7 @@ __device__ __forceinline__ void out_step(unsigned char *smem, const OutFrags &fr
     }
 }
 
-__device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, uint32_t tag, unsigned int *err,
-                                                        int &broken) {
-    // Wait until the tagged word at p carries `tag`.  Bounded: on a timeout the
-    // error word is raised and this thread stops waiting for the rest of the
-    // launch, so a lost sibling cannot stall every later chunk.
-    unsigned long long w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t n = 0;
-    while ((uint32_t)(w >> 32) != tag) {
-        if (broken || ++n > kSpinLimit) {
-            if (!broken) atomicOr(err, 1u);
-            broken = 1;
-            return 0ull;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    return w;
-}
 
-template <int N>
-__device__ __forceinline__ int modn(int x) { return ((x % N) + N) % N; }
 
 // Two-level scan: what the first pass hands the last one per (chunk slot, value head), in fp16:
 // R [64][128] (the read-out of the transition columns) as 16 MFMA A-operand fragments
@@ -995,7 +823,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int vchain = item / NSL, s = item % NSL;
         const int chain = SEG ? vchain / a.nseg : vchain, seg = SEG ? vchain % a.nseg : 0;
         const int b = chain / a.Hv, h = chain % a.Hv, kh = h / a.r;
-        const SeqInfo si = seq_info(a.cu, b, a.T, a.nch);  // the whole sequence
+        const SeqInfo si = seq_info(a.cu, b, a.T, a.nch, a.B);  // the whole sequence
         SeqInfo ss = si;                                    // the stretch this item runs over
         if (SEG) {
             const int cb = seg * a.seg_chunks;
@@ -1561,10 +1389,6 @@ struct ChainLaunch {
     int grid, ncu;
 };
 
-// Compute units left to the prep kernel before it may run beside the sequential pass, and
-// the shortest sequence (in chunks) for which it does.
-constexpr int kPrepCUs = 16;
-constexpr int kBesideMinChunks = 32;
 // Two-level scan planning: the chip's compute units (MI355X) and the shortest segment.
 constexpr int kSegChipCUs = 256;
 constexpr int kSegMinChunks = 16;
@@ -1574,8 +1398,8 @@ constexpr int kSegMinChunks = 16;
 struct DeviceFacts {
     std::mutex mu;
     int ncu = 0;
-    int chain_per_cu[2][2] = {{0, 0}, {0, 0}};  // [NT - 1][SEG]: resident chain workgroups per CU
-    int prep_lds[2] = {0, 0};                   // [THROUGH]: dynamic LDS limit set for the prep kernel
+    int seg_per_cu = 0;  // resident workgroups per CU of the two-level scan's first pass
+    int prep_lds = 0;    // dynamic LDS limit set so far for the prep kernel
 };
 
 int device_facts(DeviceFacts **out) {
@@ -1588,10 +1412,10 @@ int device_facts(DeviceFacts **out) {
     return 0;
 }
 
-template <int NT, bool SEG>
-int chain_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
-    constexpr size_t lds = ChainLds<NT>::bytes;
-    auto fn = chain_kernel<NT, SEG>;
+// Launch shape of the two-level scan's first pass (chain_kernel<2, true>).
+int seg_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
+    constexpr size_t lds = ChainLds<2>::bytes;
+    auto fn = chain_kernel<2, true>;
     DeviceFacts *df;
     int rc = device_facts(&df);
     if (rc) return rc;
@@ -1605,23 +1429,18 @@ int chain_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
             if ((e = hipDeviceGetAttribute(&df->ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
                 return fail("hipDeviceGetAttribute(multiprocessor count)", e);
         }
-        int &pc = df->chain_per_cu[NT - 1][SEG ? 1 : 0];
-        if (!pc) {
+        if (!df->seg_per_cu) {
             if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)lds)) != hipSuccess)
                 return fail("hipFuncSetAttribute(chain_kernel)", e);
-            if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pc, reinterpret_cast<const void *>(fn), 512, lds)) !=
-                hipSuccess)
+            if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&df->seg_per_cu, reinterpret_cast<const void *>(fn), 512,
+                                                                  lds)) != hipSuccess)
                 return fail("hipOccupancyMaxActiveBlocksPerMultiprocessor(chain_kernel)", e);
         }
         ncu = df->ncu;
-        per_cu = pc;
+        per_cu = df->seg_per_cu;
     }
-    constexpr int NSL = (SEG ? 2 : 1) * kTiles / NT;
-    // One workgroup per resident slot at most: a workgroup that waits for its
-    // sibling slices holds its slot, and the ticket order lets the next free
-    // slot start them.  At least 8 * NSL slots keep a started slice of every
-    // queue from blocking all slots.
+    constexpr int NSL = 2 * kTiles / 2;
     const int cap = ncu * per_cu;
     if (cap < 8 * NSL) return fail("chain_kernel: fewer resident workgroup slots than eight heads' slices");
     cl->fn = reinterpret_cast<const void *>(fn);
@@ -1633,8 +1452,9 @@ int chain_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
 
 } // namespace
 
-int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan) {
+int plan_prefill(int B, int T, int Hk, int Hv, bool packed, int segments, PrefillPlan *plan) {
     const long long chains = (long long)B * Hv;
+    // 16-column slices while the heads leave most of the chip idle, 32-column slices beyond
     const int nsl = chains <= 32 ? 8 : 4;
     plan->nslice = nsl;
     plan->nt = kTiles / nsl;
@@ -1642,24 +1462,24 @@ int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan) {
     plan->nchunks = (T + kC - 1) / kC;
     // packed: sequence b's chunks from slot floor(cu[b] / 64) + b on, all below floor(T / 64) + B
     plan->nslots = packed ? (long long)(T / kC) + B : (long long)B * plan->nchunks;
+    // one row of mailbox words per (sequence, value head, slice, ring slot), and one more set
+    // past them that the sequential pass publishes into outside a sequence's chunk range
+    plan->mbox_bytes = align256((size_t)(chains + 1) * kTiles * kRing * kC * sizeof(unsigned long long));
+    plan->xch_bytes = kHeaderBytes + plan->mbox_bytes + align256((size_t)chains * sizeof(unsigned int));
     plan->qk_bytes = align256((size_t)plan->nslots * Hk * kQKF * sizeof(_Float16));
     plan->tp_bytes = align256((size_t)plan->nslots * Hv * kTPF * sizeof(_Float16));
-    plan->ready_bytes = align256((size_t)plan->nslots * Hk * sizeof(unsigned int));
-    plan->mbox_bytes = align256((size_t)chains * kTiles * kRing * kC * sizeof(unsigned long long)) +
-                       align256((size_t)chains * sizeof(unsigned int)) + 256;
     // Two-level scan (even batches): worth it when the sequential pass would leave most of
     // the chip idle (few heads) and the sequences are long.  Its first pass runs 256 columns
     // per head in slices of 32 (measured on the shapes it is for: as many 32-column slices
     // as fit the chip beat half as many segments in 16-column slices, at about 2 us against
     // 1.25 us per chunk), so nseg segments keep B Hv 8 nseg workgroups busy; nseg fills one
-    // round of the chip.  The environment variable GDN_PREFILL_SEGMENTS overrides the
-    // choice (0 or 1: never, n >= 2: n segments).
+    // round of the chip.  `segments` overrides the choice (1: never, n >= 2: n segments).
     plan->nseg = 1;
     plan->seg_chunks = plan->nchunks;
     if (!packed) {
         long long want = 0;
-        if (const char *e = std::getenv("GDN_PREFILL_SEGMENTS"))
-            want = std::atoll(e);
+        if (segments > 0)
+            want = segments;
         else if (chains * nsl * 4 <= kSegChipCUs)  // the sequential pass would use at most a quarter of the chip
             want = std::min<long long>(kSegChipCUs / (chains * 8), plan->nchunks / kSegMinChunks);
         want = std::min<long long>(want, plan->nchunks);
@@ -1678,174 +1498,103 @@ int plan_prefill(int B, int T, int Hk, int Hv, bool packed, PrefillPlan *plan) {
         plan->seg_state_bytes = align256(vchains * kD * 2 * kD * sizeof(float));
         plan->seg_frag_bytes = align256(vchains * kTiles * 4 * kFrag * sizeof(_Float16));
     }
-    plan->total_bytes = plan->qk_bytes + plan->tp_bytes + plan->ready_bytes + plan->mbox_bytes +
-                        plan->seg_out_bytes + plan->seg_state_bytes + plan->seg_frag_bytes;
+    plan->total_bytes = plan->xch_bytes + plan->qk_bytes + plan->tp_bytes + plan->seg_out_bytes +
+                        plan->seg_state_bytes + plan->seg_frag_bytes;
     return 0;
 }
 
-namespace {
-
-// A second stream per device for the prep kernel, so that it can run beside the
-// sequential pass on the compute units the latter leaves free, and two events
-// that order it with the caller's stream.  Created on first use, kept for the
-// life of the process, default priority.
-// The enqueue sequence that uses them runs under the device's lock, so that
-// calls from several host threads cannot interleave their event records.
-struct SideStream {
-    std::mutex mu;
-    hipStream_t s = nullptr;
-    hipEvent_t in = nullptr, done = nullptr;
-};
-
-// Returns the device's side stream (created on first use); the caller holds ss->mu.
-int side_stream(int dev, SideStream **out) {
-    static SideStream per_dev[64];
-    if (dev < 0 || dev >= 64) return fail("prefill: device index out of range for the side stream");
-    SideStream &ss = per_dev[dev];
-    if (!ss.s) {
-        hipError_t e;
-        if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess)
-            return fail("hipStreamCreateWithFlags(prep stream)", e);
-        if ((e = hipEventCreateWithFlags(&ss.in, hipEventDisableTiming)) != hipSuccess)
-            return fail("hipEventCreateWithFlags", e);
-        if ((e = hipEventCreateWithFlags(&ss.done, hipEventDisableTiming)) != hipSuccess)
-            return fail("hipEventCreateWithFlags", e);
-    }
-    *out = &ss;
-    return 0;
+PrefillRegions prefill_regions(void *workspace, const PrefillPlan &plan, int B, int Hv) {
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    PrefillRegions r;
+    r.err = reinterpret_cast<unsigned int *>(ws + kErrOffset);
+    r.tickets = reinterpret_cast<unsigned int *>(ws + kTicketOffset);
+    r.exits = reinterpret_cast<unsigned int *>(ws + kExitOffset);
+    r.mbox = reinterpret_cast<unsigned long long *>(ws + kHeaderBytes);
+    r.counters = reinterpret_cast<unsigned int *>(ws + kHeaderBytes + plan.mbox_bytes);
+    r.qkf = reinterpret_cast<_Float16 *>(ws + plan.xch_bytes);
+    r.tpf = reinterpret_cast<_Float16 *>(ws + plan.xch_bytes + plan.qk_bytes);
+    r.seg = ws + plan.xch_bytes + plan.qk_bytes + plan.tp_bytes;
+    (void)B;
+    (void)Hv;
+    return r;
 }
 
-// Running the two kernels side by side needs the device to run them at the same
-// time.  A counter-collecting profiler (rocprofv3 --pmc, which sets
-// ROCPROF_COUNTERS) serialises every dispatch and may start the sequential pass
-// first, which would then wait out its bounded waits for stamps that cannot come;
-// such runs, and any run with GDN_PREFILL_SEQUENTIAL set, use one stream.
-bool beside_allowed() {
-    static const bool ok = !std::getenv("ROCPROF_COUNTERS") && !std::getenv("GDN_PREFILL_SEQUENTIAL");
-    return ok;
-}
-
-} // namespace
-
+// Two kernels one after the other on the caller's stream: the prep kernel (every chunk of
+// every key head in parallel; it also clears the workspace's exchange area), then the
+// sequential pass, whose workgroups only ever wait for sibling workgroups of the same
+// launch.  With the two-level scan the sequential pass is its first pass, followed by the
+// combine and output kernels.
 int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t stream) {
-    unsigned char *ws = static_cast<unsigned char *>(p.workspace);
-    _Float16 *qkf = reinterpret_cast<_Float16 *>(ws);
-    _Float16 *tpf = reinterpret_cast<_Float16 *>(ws + plan.qk_bytes);
-    unsigned int *ready = reinterpret_cast<unsigned int *>(ws + plan.qk_bytes + plan.tp_bytes);
-    // the two-level scan's regions (if any), then the exchange area, whose last 256 bytes hold
-    // the error word at the very end of the workspace
-    unsigned char *sgb = ws + plan.qk_bytes + plan.tp_bytes + plan.ready_bytes;
-    unsigned char *mb = sgb + plan.seg_out_bytes + plan.seg_state_bytes + plan.seg_frag_bytes;
+    const PrefillRegions rg = prefill_regions(p.workspace, plan, p.B, p.Hv);
     const size_t chains = (size_t)p.B * p.Hv;
-    const size_t mbox_sz = align256(chains * kTiles * kRing * kC * sizeof(unsigned long long));
-    unsigned int *counters = reinterpret_cast<unsigned int *>(mb + mbox_sz);
-    // last 256 bytes: error word, then the eight queue tickets and the exit count
-    unsigned int *err = reinterpret_cast<unsigned int *>(mb + mbox_sz + align256(chains * sizeof(unsigned int)));
-    // Every call gets a stamp no earlier call in this process had; a zero-filled
-    // workspace holds none (stamps start at 1 and compare modulo 2^32).
-    static std::atomic<unsigned int> call_count{0};
-    unsigned int stamp = call_count.fetch_add(1u) + 1u;
-    if (stamp == 0u) stamp = call_count.fetch_add(1u) + 1u;
+    hipError_t e;
+    int rc;
 
     PrepArgs pa;
     pa.q = p.q; pa.k = p.k; pa.conv_w = p.conv_w; pa.conv_state_in = p.conv_state_in;
     pa.g = p.g; pa.beta = p.beta; pa.A_log = p.A_log; pa.dt_bias = p.dt_bias; pa.conv_state_out = p.conv_state_out;
-    pa.qkf = qkf; pa.tpf = tpf; pa.ready = ready; pa.stamp = stamp; pa.cu = p.cu_seqlens;
+    pa.qkf = rg.qkf; pa.tpf = rg.tpf; pa.cu = p.cu_seqlens;
+    pa.clear = reinterpret_cast<uint4 *>(p.workspace); pa.clear_n16 = plan.xch_bytes / 16;
     pa.B = p.B; pa.T = p.T; pa.Hk = p.Hk; pa.Hv = p.Hv; pa.r = p.Hv / p.Hk;
     pa.Cc = 2 * p.Hk * kD + p.Hv * kD; pa.conv = p.conv_width == 4; pa.nch = plan.nchunks;
     pa.eps_l2 = p.eps_l2;
-
-    ChainArgs a;
-    a.qkf = qkf; a.tpf = tpf;
-    a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w; a.conv_state_in = p.conv_state_in;
-    a.state_in = p.state_in; a.o = p.o; a.conv_state_out = p.conv_state_out; a.state_out = p.state_out;
-    a.mbox = reinterpret_cast<unsigned long long *>(mb); a.counters = counters; a.err = err;
-    a.tickets = err + 16; a.exits = err + 32; a.ready = ready; a.stamp = stamp; a.cu = p.cu_seqlens; a.check = 1;
-    a.B = p.B; a.T = p.T; a.Hk = p.Hk; a.Hv = p.Hv; a.r = pa.r; a.Cc = pa.Cc; a.conv = pa.conv; a.norm = p.norm;
-    a.nch = plan.nchunks; a.n_items = (int)(chains * plan.nslice); a.grid = 0;
-    a.eps_norm = p.eps_norm;
-
-    const bool seg = plan.nseg > 1;
-    a.seg_out = seg ? reinterpret_cast<_Float16 *>(sgb) : nullptr;
-    a.seg_state = seg ? reinterpret_cast<float *>(sgb + plan.seg_out_bytes) : nullptr;
-    a.nseg = plan.nseg; a.seg_chunks = plan.seg_chunks;
-    if (seg) a.n_items = (int)(chains * plan.nseg * 2 * plan.nslice);
-
-    ChainLaunch cl;
-    int rc = plan.nt == 1 ? (seg ? chain_launch_shape<1, true>(a, &cl) : chain_launch_shape<1, false>(a, &cl))
-             : plan.nt == 2 ? (seg ? chain_launch_shape<2, true>(a, &cl) : chain_launch_shape<2, false>(a, &cl))
-                            : fail("prefill plan: unsupported value-tile count");
-    if (rc) return rc;
-    a.grid = cl.grid;
-
-    // The prep kernel runs beside the sequential pass when the latter leaves
-    // compute units free (it never waits for the sequential pass, so it always
-    // finishes); otherwise the two run one after the other on the caller's stream.
-    // Prep is enqueued first either way: if both streams share a hardware queue,
-    // the sequential pass simply starts after it.
-    // (The two-level scan's first pass starts every segment at once, so it runs after prep.
-    // Short sequences run one kernel after the other too: the overlap then saves less than
-    // the two events and stream waits it costs on the host.)
-    const bool beside = !seg && plan.nchunks >= kBesideMinChunks && cl.grid + kPrepCUs <= cl.ncu && beside_allowed();
-    a.check = beside ? 1 : 0;
-    hipStream_t ps = stream;
-    SideStream *ss = nullptr;
-    std::unique_lock<std::mutex> lock;
-    hipError_t e;
-    if (beside) {
-        int dev = 0;
-        if ((e = hipGetDevice(&dev)) != hipSuccess) return fail("hipGetDevice", e);
-        static std::mutex create_mu;
-        {
-            std::lock_guard<std::mutex> g(create_mu);
-            if ((rc = side_stream(dev, &ss))) return rc;
-        }
-        lock = std::unique_lock<std::mutex>(ss->mu);
-        if ((e = hipEventRecord(ss->in, stream)) != hipSuccess) return fail("hipEventRecord", e);
-        if ((e = hipStreamWaitEvent(ss->s, ss->in, 0)) != hipSuccess) return fail("hipStreamWaitEvent", e);
-        ps = ss->s;
-    }
     const size_t plds = PrepLds::bytes(pa.r);
-    const void *prep_fn = beside ? reinterpret_cast<const void *>(chunk_prep_kernel<true>)
-                                 : reinterpret_cast<const void *>(chunk_prep_kernel<false>);
+    const void *prep_fn = reinterpret_cast<const void *>(chunk_prep_kernel);
     {   // raise the prep kernel's LDS limit when this head ratio needs more than set so far
         DeviceFacts *df;
         if ((rc = device_facts(&df))) return rc;
         std::lock_guard<std::mutex> g(df->mu);
-        int &lim = df->prep_lds[beside ? 1 : 0];
-        if ((int)plds > lim) {
+        if ((int)plds > df->prep_lds) {
             if ((e = hipFuncSetAttribute(prep_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)plds)) != hipSuccess)
                 return fail("hipFuncSetAttribute(chunk_prep_kernel)", e);
-            lim = (int)plds;
+            df->prep_lds = (int)plds;
         }
     }
     void *pargs[] = {&pa};
-    if ((e = hipLaunchKernel(prep_fn,
-                             dim3((unsigned)(plan.nslots * p.Hk)), dim3(256), pargs, plds, ps)) !=
+    if ((e = hipLaunchKernel(prep_fn, dim3((unsigned)(plan.nslots * p.Hk)), dim3(256), pargs, plds, stream)) !=
         hipSuccess)
         return fail("hipLaunchKernel(chunk_prep_kernel)", e);
-    if (beside && (e = hipEventRecord(ss->done, ps)) != hipSuccess) return fail("hipEventRecord", e);
+
+    if (plan.nseg <= 1) return launch_pass(p, plan, rg, stream);
+
+    // ---- two-level scan
+    ChainArgs a;
+    a.qkf = rg.qkf; a.tpf = rg.tpf;
+    a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w; a.conv_state_in = p.conv_state_in;
+    a.state_in = p.state_in; a.o = p.o; a.conv_state_out = p.conv_state_out; a.state_out = p.state_out;
+    a.mbox = rg.mbox; a.counters = rg.counters; a.err = rg.err;
+    a.tickets = rg.tickets; a.exits = rg.exits;
+    // the prep kernel has finished before this launch starts: the load wave's readiness loads
+    // read valid memory (the operand blocks) and their values are never tested (check = 0)
+    a.ready = reinterpret_cast<const unsigned int *>(rg.qkf); a.stamp = 0; a.check = 0;
+    a.cu = p.cu_seqlens;
+    a.B = p.B; a.T = p.T; a.Hk = p.Hk; a.Hv = p.Hv; a.r = pa.r; a.Cc = pa.Cc; a.conv = pa.conv; a.norm = p.norm;
+    a.nch = plan.nchunks; a.grid = 0;
+    a.eps_norm = p.eps_norm;
+    a.seg_out = reinterpret_cast<_Float16 *>(rg.seg);
+    a.seg_state = reinterpret_cast<float *>(rg.seg + plan.seg_out_bytes);
+    a.nseg = plan.nseg; a.seg_chunks = plan.seg_chunks;
+    a.n_items = (int)(chains * plan.nseg * 2 * plan.nslice);
+    ChainLaunch cl;
+    if ((rc = seg_launch_shape(a, &cl))) return rc;
+    a.grid = cl.grid;
     void *cargs[] = {&a};
     if ((e = hipLaunchKernel(cl.fn, dim3(cl.grid), dim3(512), cargs, cl.lds, stream)) != hipSuccess)
         return fail("hipLaunchKernel(chain_kernel)", e);
-    if (seg) {
-        SegArgs sa;
-        sa.state_in = p.state_in; sa.seg_state = a.seg_state;
-        sa.seg_frag = reinterpret_cast<_Float16 *>(sgb + plan.seg_out_bytes + plan.seg_state_bytes);
-        sa.state_out = p.state_out; sa.seg_out = a.seg_out; sa.z = p.z; sa.norm_w = p.norm_w; sa.o = p.o;
-        sa.B = p.B; sa.T = p.T; sa.Hv = p.Hv; sa.nch = plan.nchunks; sa.nseg = plan.nseg;
-        sa.seg_chunks = plan.seg_chunks; sa.norm = p.norm; sa.eps_norm = p.eps_norm;
-        void *sargs[] = {&sa};
-        if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_combine_kernel), dim3((unsigned)(chains * kTiles)),
-                                 dim3(256), sargs, 0, stream)) != hipSuccess)
-            return fail("hipLaunchKernel(seg_combine_kernel)", e);
-        if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_output_kernel),
-                                 dim3((unsigned)((size_t)p.B * plan.nchunks * p.Hv)), dim3(256), sargs, 0, stream)) !=
-            hipSuccess)
-            return fail("hipLaunchKernel(seg_output_kernel)", e);
-    }
-    // the caller's stream completes only after both kernels
-    if (beside && (e = hipStreamWaitEvent(stream, ss->done, 0)) != hipSuccess) return fail("hipStreamWaitEvent", e);
+    SegArgs sa;
+    sa.state_in = p.state_in; sa.seg_state = a.seg_state;
+    sa.seg_frag = reinterpret_cast<_Float16 *>(rg.seg + plan.seg_out_bytes + plan.seg_state_bytes);
+    sa.state_out = p.state_out; sa.seg_out = a.seg_out; sa.z = p.z; sa.norm_w = p.norm_w; sa.o = p.o;
+    sa.B = p.B; sa.T = p.T; sa.Hv = p.Hv; sa.nch = plan.nchunks; sa.nseg = plan.nseg;
+    sa.seg_chunks = plan.seg_chunks; sa.norm = p.norm; sa.eps_norm = p.eps_norm;
+    void *sargs[] = {&sa};
+    if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_combine_kernel), dim3((unsigned)(chains * kTiles)),
+                             dim3(256), sargs, 0, stream)) != hipSuccess)
+        return fail("hipLaunchKernel(seg_combine_kernel)", e);
+    if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_output_kernel),
+                             dim3((unsigned)((size_t)p.B * plan.nchunks * p.Hv)), dim3(256), sargs, 0, stream)) !=
+        hipSuccess)
+        return fail("hipLaunchKernel(seg_output_kernel)", e);
     return 0;
 }
 

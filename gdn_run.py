@@ -32,8 +32,8 @@ class Prefill:
     """Device buffers of one prefill call: inputs, outputs and workspace."""
 
     def __init__(self, inp: dict, B: int, T: int, Hk: int, Hv: int, conv: bool, norm: bool,
-                 state_in=None, conv_state_in=None, want_conv_state: bool = True):
-        self.shape = gdn.make_shape(B, T, Hk, Hv, conv=conv, norm=norm)
+                 state_in=None, conv_state_in=None, want_conv_state: bool = True, segments: int = 0):
+        self.shape = gdn.make_shape(B, T, Hk, Hv, conv=conv, norm=norm, segments=segments)
         self.B, self.T, self.Hk, self.Hv, self.conv, self.norm = B, T, Hk, Hv, conv, norm
         self.d = {n: to_dev(inp.get(n)) for n in ("q", "k", "v", "g", "beta")}
         self.d["z"] = to_dev(inp.get("z")) if norm else None
@@ -67,8 +67,9 @@ class Prefill:
                                     self.state_out, self.conv_state_out, self.ws, self.ws_bytes, stream=stream)
 
     def exchange_error_word(self) -> int:
-        """Last 32-bit word area of the workspace: non-zero if a bounded wait timed out."""
-        return int(self.ws[-256:-252].view(torch.int32).item())
+        """The workspace's error word (its first 32-bit word): bit 0 a bounded wait timed out,
+        bit 1 a packed sequence was skipped."""
+        return int(self.ws[0:4].view(torch.int32).item())
 
 
 class PackedPrefill:
@@ -113,7 +114,7 @@ class PackedPrefill:
                                            self.conv_state_out, self.ws, self.ws_bytes, stream=stream)
 
     def exchange_error_word(self) -> int:
-        return int(self.ws[-256:-252].view(torch.int32).item())
+        return int(self.ws[0:4].view(torch.int32).item())
 
 
 class Decode:

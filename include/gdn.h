@@ -26,9 +26,9 @@
  * Conventions for every call.
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous; bf16
  *    tensors are passed as uint16_t bit patterns.  The caller owns every
- *    buffer.  The library allocates no device memory and never synchronises
- *    (the first prefill on a device creates one side stream and two events,
- *    kept until the process ends; see gdn_prefill).
+ *    buffer.  The library allocates no device memory, keeps no per-call state
+ *    between calls, and never synchronises (gdn_prefill_check, which waits on
+ *    the stream it is given, is the one exception, and says so).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it; results are visible once the caller syncs it.
  *  - Every argument is checked on the host before any HIP call; a failed
@@ -54,6 +54,8 @@ extern "C" {
 #define GDN_EUNSUPPORTED (-2) /* a head width other than 128, a conv width other than 0/4 */
 #define GDN_EHIP (-3)        /* a HIP call or kernel launch failed */
 #define GDN_EWORKSPACE (-4)  /* workspace too small */
+#define GDN_ETIMEOUT (-5)    /* gdn_prefill_check: a bounded wait between workgroups timed out; outputs are wrong */
+#define GDN_ESKIPPED (-6)    /* gdn_prefill_check: a packed sequence with invalid bounds was skipped */
 
 /* flags */
 #define GDN_NO_NORM 1u /* return the raw read-out o instead of the gated RMSNorm (z, norm_w unused) */
@@ -70,6 +72,10 @@ typedef struct gdn_shape {
     uint32_t flags;     /* GDN_NO_NORM, GDN_PACKED (prefill only), both or 0 */
     float eps_l2;       /* eps inside the q/k L2-norm root (1e-6 on the pages) */
     float eps_norm;     /* eps of the gated RMSNorm (1e-6 on the pages) */
+    int32_t prefill_segments; /* prefill of an even batch: 0 lets the library choose, 1 runs the plain
+                                 sequential pass, n >= 2 splits every sequence into n segments (the
+                                 two-level scan; capped at the chunk count); must be 0 or 1 with
+                                 GDN_PACKED; ignored by the decode calls */
 } gdn_shape;
 
 /*
@@ -83,16 +89,16 @@ int gdn_state_init(const gdn_shape *shape, float *state, uint16_t *conv_state, v
 /*
  * Bytes of device workspace gdn_prefill (gdn_prefill_packed, when the shape
  * carries GDN_PACKED) needs for `shape` (written to *bytes).
- * The workspace holds the state-independent chunk operands that one kernel
- * computes for the sequential pass of another: the normalised q/k rows (fp16,
- * B*T*Hk*2*Dk values), per (chunk, value head) the packed lower-triangular
- * T diag(beta) and (Q K^T) o R blocks and the decay vectors ("How Qwen3.5
- * works" §9.11), one readiness word per (sequence, chunk, key head) through
- * which the sequential pass follows the kernel that computes those operands
- * (the two may run at the same time), and an exchange area: the per-row sums
- * of squares that the workgroups sharing one head trade for the gated RMSNorm,
- * work-queue tickets and an error word.  Returns GDN_EINVAL for a shape
- * gdn_prefill would reject.
+ * The workspace starts with a 256-byte header whose first 32-bit word is the
+ * error word (see gdn_prefill_check), then the exchange area the workgroups of
+ * one head trade through (the per-row sums of squares the gated RMSNorm needs
+ * from every value slice, and work-queue tickets), then the state-independent
+ * chunk operands that the first kernel of a call computes for the sequential
+ * pass ("How Qwen3.5 works" §9.11): the normalised q/k rows in both the row and
+ * the transposed fragment order (fp16, 3*B*T*Hk*Dk values), and per (chunk,
+ * value head) the packed lower-triangular T diag(beta) and (Q K^T) o R blocks
+ * and the decay vectors.  Returns GDN_EINVAL for a shape gdn_prefill would
+ * reject.
  */
 int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
 
@@ -107,8 +113,8 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
  * S), so each segment is run from zero together with its transition map, the
  * maps are chained, and what each start state adds to the outputs is applied
  * last.  The workspace is then larger (gdn_prefill_workspace_size accounts for
- * it).  The environment variable GDN_PREFILL_SEGMENTS, read at every call,
- * overrides the choice: 0 or 1 never splits, n >= 2 asks for n segments.
+ * it).  shape->prefill_segments overrides the choice: 1 never splits, n >= 2
+ * asks for n segments.
  *
  *  q, k           [B][T][Hk][128] bf16
  *  v, z           [B][T][Hv][128] bf16 (z may be NULL iff GDN_NO_NORM)
@@ -121,17 +127,16 @@ int gdn_prefill_workspace_size(const gdn_shape *shape, size_t *bytes);
  *  state_out      [B][Hv][128][128] fp32 output; may be the same buffer as state_in
  *  conv_state_out [B][3][Cc] bf16, the raw inputs of the last three tokens, or
  *                 NULL; must not overlap conv_state_in
- *  workspace      device memory of at least gdn_prefill_workspace_size() bytes.
- *                 It must be zero-filled before its first use; every call that
- *                 completes leaves its exchange area zeroed again and its
- *                 readiness words holding a per-call stamp that no later call
- *                 in the process reuses (stamps wrap after 2^31 calls).  Calls
- *                 that run concurrently must not share a workspace.  The one
- *                 exception to the clean exchange area is the error word, the
- *                 first 32-bit word of the workspace's last 256 bytes: bit 0 says
- *                 a bounded cross-workgroup wait timed out (the outputs are then
- *                 wrong), bit 1 that gdn_prefill_packed skipped a sequence with
- *                 invalid bounds.  It keeps its bits until the caller clears it.
+ *  workspace      device memory of at least gdn_prefill_workspace_size() bytes,
+ *                 16-byte aligned, with no required contents: every call clears
+ *                 the header and the exchange area before anything reads them
+ *                 and overwrites the operand blocks.  Calls that may run at the
+ *                 same time must not share a workspace.  After the call its error
+ *                 word (the first 32-bit word) holds this call's error bits: bit 0
+ *                 says a bounded wait between workgroups timed out (the affected
+ *                 output rows are then NaN and the call's results are wrong),
+ *                 bit 1 that gdn_prefill_packed skipped a sequence with invalid
+ *                 bounds.
  *
  * `o` must not overlap any input.  Returns GDN_OK once the work is enqueued.
  */
@@ -141,6 +146,20 @@ int gdn_prefill(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
                 const uint16_t *conv_state_in, uint16_t *o, float *state_out,
                 uint16_t *conv_state_out, void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/*
+ * Wait for `stream` and read the error word that the last prefill call on
+ * `workspace` left (the calls above never wait; this one synchronises the
+ * stream, so call it when the results are needed anyway).  Returns GDN_OK when
+ * the word is zero, GDN_ETIMEOUT when a bounded wait between workgroups timed
+ * out (the outputs are wrong: the rows it affected are NaN), GDN_ESKIPPED when
+ * only a packed sequence with invalid bounds was skipped, GDN_EINVAL for a null
+ * workspace or one smaller than 256 bytes, GDN_EHIP if the wait or the copy
+ * failed.  "How Qwen3.5 works" §9.10's reference loop rejects bad input rather
+ * than returning quietly wrong results; this is how a caller learns of the
+ * failures that only the device can see.
+ */
+int gdn_prefill_check(const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One decode step: one new token per sequence, updating the recurrent state

@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["gdn_decode_step", "gdn_decode_step_gate_logits", "gdn_last_error", "gdn_prefill",
          "gdn_prefill_gate_logits", "gdn_prefill_packed", "gdn_prefill_packed_gate_logits",
-         "gdn_decode_multi", "gdn_decode_multi_gate_logits",
+         "gdn_decode_multi", "gdn_decode_multi_gate_logits", "gdn_prefill_check",
          "gdn_prefill_workspace_size", "gdn_state_init", "gdn_status_string"])
 
 
@@ -276,28 +276,26 @@ def test_one_hip_runtime_per_process():
     assert out.strip() == "1"
 
 
-def test_two_level_plan_sizes_the_workspace(monkeypatch):
+def test_two_level_plan_sizes_the_workspace():
     """Few heads and a long sequence: the plan splits the sequence into segments, and the
     workspace grows by their read-outs (32 KB per chunk and head) and segment maps.  The
     benchmark shapes (16 or more heads) and packed batches keep the plain sequential pass."""
-    few = _shape(B=1, T=262144, Hk=1, Hv=3)
-    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
-    plain = gdn.gdn_prefill_workspace_size(few)
-    monkeypatch.delenv("GDN_PREFILL_SEGMENTS")
-    planned = gdn.gdn_prefill_workspace_size(few)
+    plain = gdn.gdn_prefill_workspace_size(_shape(B=1, T=262144, Hk=1, Hv=3, segments=1))
+    planned = gdn.gdn_prefill_workspace_size(_shape(B=1, T=262144, Hk=1, Hv=3))
     assert planned - plain >= (262144 // 64) * 3 * 32 * 1024
-    for s in (_shape(B=1, T=4096, Hk=16, Hv=16), _shape(B=4, T=16384, Hk=16, Hv=32),
-              _shape(B=3, T=65536, Hk=1, Hv=3, packed=True)):
-        monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
-        a = gdn.gdn_prefill_workspace_size(s)
-        monkeypatch.delenv("GDN_PREFILL_SEGMENTS")
-        assert gdn.gdn_prefill_workspace_size(s) == a
+    for kw in (dict(B=1, T=4096, Hk=16, Hv=16), dict(B=4, T=16384, Hk=16, Hv=32),
+               dict(B=3, T=65536, Hk=1, Hv=3, packed=True)):
+        assert gdn.gdn_prefill_workspace_size(_shape(**kw)) == gdn.gdn_prefill_workspace_size(_shape(**kw, segments=1))
     # a forced split asks for more only when the sequence has more than one chunk
-    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
-    short_plain = gdn.gdn_prefill_workspace_size(_shape(B=1, T=1000, Hk=1, Hv=3))
-    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "4")
-    assert gdn.gdn_prefill_workspace_size(_shape(B=1, T=1000, Hk=1, Hv=3)) > short_plain
-    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "0")
-    one_chunk = gdn.gdn_prefill_workspace_size(_shape(B=1, T=64, Hk=1, Hv=3))
-    monkeypatch.setenv("GDN_PREFILL_SEGMENTS", "4")
-    assert gdn.gdn_prefill_workspace_size(_shape(B=1, T=64, Hk=1, Hv=3)) == one_chunk
+    short_plain = gdn.gdn_prefill_workspace_size(_shape(B=1, T=1000, Hk=1, Hv=3, segments=1))
+    assert gdn.gdn_prefill_workspace_size(_shape(B=1, T=1000, Hk=1, Hv=3, segments=4)) > short_plain
+    one_chunk = gdn.gdn_prefill_workspace_size(_shape(B=1, T=64, Hk=1, Hv=3, segments=1))
+    assert gdn.gdn_prefill_workspace_size(_shape(B=1, T=64, Hk=1, Hv=3, segments=4)) == one_chunk
+
+
+def test_segment_field_is_checked():
+    """prefill_segments must not be negative, and a packed batch takes no forced split."""
+    n = C.c_size_t(0)
+    assert gdn._lib.gdn_prefill_workspace_size(C.byref(_shape(segments=-1)), C.byref(n)) == gdn.GDN_EINVAL
+    assert gdn._lib.gdn_prefill_workspace_size(C.byref(_shape(packed=True, segments=2)), C.byref(n)) == gdn.GDN_EINVAL
+    assert gdn._lib.gdn_prefill_workspace_size(C.byref(_shape(packed=True, segments=1)), C.byref(n)) == gdn.GDN_OK

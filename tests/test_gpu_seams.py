@@ -182,39 +182,25 @@ def test_state_init_zeroes():
     assert int(torch.count_nonzero(st)) == 0
 
 
-_SEQ_CHILD = r"""
-import sys, numpy as np
-sys.path.insert(0, sys.argv[1])
-import gdn_inputs as GI
-import gdn_run as R
-import torch
-w = GI.Workload("seq_mode", 2, 200, 2, 4, random_state=True, random_conv_state=True, tag=703)
-r = R.Prefill(GI.make_inputs(w), 2, 200, 2, 4, True, True)
-r.run()
-torch.cuda.synchronize()
-assert r.exchange_error_word() == 0
-np.savez(sys.argv[2], o=R.bits(r.o), s=r.state_out.cpu().numpy(), cs=R.bits(r.conv_state_out))
-"""
-
-
-def test_sequential_mode_matches_side_by_side(tmp_path):
-    """GDN_PREFILL_SEQUENTIAL=1 (one stream, prep then chain) gives the same bits as
-    the default, where the prep kernel may run beside the sequential pass."""
+def test_workspace_reused_across_shapes_matches_fresh_workspace():
+    """One workspace serves a long call and then a shorter one of another shape: every call
+    clears the exchange area it uses (queue tickets, mailbox, error word) before reading it,
+    so the second call's results equal those on a fresh, zero-filled workspace."""
     R = _R()
-    import os
-    import subprocess
-    import sys
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    out = str(tmp_path / "seq.npz")
-    env = dict(os.environ, GDN_PREFILL_SEQUENTIAL="1")
-    print("[seam] sequential-mode child process", flush=True)
-    subprocess.run([sys.executable, "-c", _SEQ_CHILD, root, out], env=env, check=True, timeout=300)
-    w = GI.Workload("seq_mode", 2, 200, 2, 4, random_state=True, random_conv_state=True, tag=703)
-    r = R.Prefill(GI.make_inputs(w), 2, 200, 2, 4, True, True)
-    r.run()
+    wa = GI.Workload("ws_long", 1, 4096, 16, 16, random_state=True, random_conv_state=True, tag=705)
+    wb = GI.Workload("ws_short", 2, 1000, 2, 6, random_state=True, random_conv_state=True, tag=706)
+    a = R.Prefill(GI.make_inputs(wa), 1, 4096, 16, 16, True, True)
+    b = R.Prefill(GI.make_inputs(wb), 2, 1000, 2, 6, True, True)
+    fresh = R.Prefill(GI.make_inputs(wb), 2, 1000, 2, 6, True, True)
+    assert a.ws_bytes >= b.ws_bytes
+    b.ws, b.ws_bytes = a.ws, a.ws_bytes  # b runs on the (larger) workspace a has just used
+    a.run()
+    b.run()
+    fresh.run()
     torch.cuda.synchronize()
-    assert r.exchange_error_word() == 0
-    ref = np.load(out)
-    np.testing.assert_array_equal(R.bits(r.o), ref["o"])
-    np.testing.assert_array_equal(r.state_out.cpu().numpy(), ref["s"])
-    np.testing.assert_array_equal(R.bits(r.conv_state_out), ref["cs"])
+    assert a.exchange_error_word() == 0 and b.exchange_error_word() == 0
+    assert torch.equal(b.o, fresh.o)
+    assert torch.equal(b.state_out, fresh.state_out)
+    assert torch.equal(b.conv_state_out, fresh.conv_state_out)
+    import gated_deltanet_mixer_amd as gdn
+    gdn.gdn_prefill_check(a.ws)  # the checked form of the same error word

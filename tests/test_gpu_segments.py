@@ -6,16 +6,13 @@ segments: a first pass runs all segments at once, each from a zero state plus
 a second pass chains the segment maps in fp32, and a third adds what the start
 states contribute to the outputs and applies the gated RMSNorm.  The results
 must match the oracle's token-by-token recurrence to the same tolerances as
-the plain sequential pass.  GDN_PREFILL_SEGMENTS forces a segment count (0:
-never split) so that small shapes exercise every part.
+the plain sequential pass.  The shape's prefill_segments field forces a segment
+count (1: never split) so that small shapes exercise every part.
 
 The long-memory cases (decay near 1: a state half-life of 200k tokens, far
 longer than the sequence) check that nothing in either path loses precision
 when the state keeps everything it has seen.
 """
-import contextlib
-import os
-
 import numpy as np
 import pytest
 
@@ -36,27 +33,10 @@ def _R():
     return gdn_run
 
 
-@contextlib.contextmanager
-def segments(n):
-    old = os.environ.get("GDN_PREFILL_SEGMENTS")
-    if n is None:
-        os.environ.pop("GDN_PREFILL_SEGMENTS", None)
-    else:
-        os.environ["GDN_PREFILL_SEGMENTS"] = str(n)
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("GDN_PREFILL_SEGMENTS", None)
-        else:
-            os.environ["GDN_PREFILL_SEGMENTS"] = old
-
-
 def _run_and_check(R, inp, B, T, Hk, Hv, conv, norm, nseg, label):
-    with segments(nseg):
-        run = R.Prefill(inp, B, T, Hk, Hv, conv, norm)
-        run.run()
-        torch.cuda.synchronize()
+    run = R.Prefill(inp, B, T, Hk, Hv, conv, norm, segments=0 if nseg is None else nseg)
+    run.run()
+    torch.cuda.synchronize()
     assert run.exchange_error_word() == 0
     y_ref, S_ref, cs_ref = O.prefill(inp, B, T, Hk, Hv, conv, norm)
     o = R.bits(run.o).reshape(B, T, Hv, D)
@@ -94,7 +74,7 @@ def test_segments_match_plain_pass_closely():
     B, T, Hk, Hv = 1, 2048, 1, 2
     w = GI.Workload("seg_vs_plain", B, T, Hk, Hv, random_state=True, random_conv_state=True, tag=1520)
     inp = GI.make_inputs(w)
-    a = _run_and_check(R, inp, B, T, Hk, Hv, True, True, 0, "plain")
+    a = _run_and_check(R, inp, B, T, Hk, Hv, True, True, 1, "plain")
     b = _run_and_check(R, inp, B, T, Hk, Hv, True, True, 8, "8 segments")
     assert b.ws_bytes > a.ws_bytes  # the segment plan ran (its read-outs and maps live in the workspace)
     print(f"[segments] outputs bit-equal: {torch.equal(a.o, b.o)}, states bit-equal: "
@@ -103,7 +83,7 @@ def test_segments_match_plain_pass_closely():
     assert state_error(sb, sa.astype(np.float64)) <= STATE_TOL
 
 
-@pytest.mark.parametrize("nseg", [0, 8])
+@pytest.mark.parametrize("nseg", [1, 8])
 def test_long_memory_stress(nseg):
     """Decay near 1 (alpha = 2^(-1/200000): the state halves only after 200k tokens), T = 32768:
     the state keeps every write, through the plain pass and the two-level scan."""
@@ -124,10 +104,9 @@ def test_segments_with_gate_logits():
     inp = GI.make_inputs(w)
     gl = GI.make_gate_logits(w)
     g, beta = O.gate_logits(gl["a"], gl["b"], gl["A_log"], gl["dt_bias"])
-    with segments(4):
-        run = R.Prefill(inp, B, T, Hk, Hv, True, True)
-        run.run_gate_logits(gl)
-        torch.cuda.synchronize()
+    run = R.Prefill(inp, B, T, Hk, Hv, True, True, segments=4)
+    run.run_gate_logits(gl)
+    torch.cuda.synchronize()
     assert run.exchange_error_word() == 0
     ref_inp = dict(inp, g=g.astype(np.float32), beta=beta.astype(np.float32))
     y_ref, S_ref, cs_ref = O.prefill(ref_inp, B, T, Hk, Hv, True, True)

@@ -69,17 +69,10 @@ def test_sweep_prefill(c):
     inp = GI.make_inputs(w)
     label = f"prefill {c}"
     print(f"[sweep] {label}", flush=True)
-    old = os.environ.get("GDN_PREFILL_SEGMENTS")
-    os.environ["GDN_PREFILL_SEGMENTS"] = str(c["nseg"])
-    try:
-        run = R.Prefill(inp, B, T, Hk, Hv, conv, norm)
-        run.run()
-        torch.cuda.synchronize()
-    finally:
-        if old is None:
-            os.environ.pop("GDN_PREFILL_SEGMENTS", None)
-        else:
-            os.environ["GDN_PREFILL_SEGMENTS"] = old
+    # segment count: 0 draws the plain sequential pass (forced with 1), n >= 2 n segments
+    run = R.Prefill(inp, B, T, Hk, Hv, conv, norm, segments=max(1, c["nseg"]))
+    run.run()
+    torch.cuda.synchronize()
     assert run.exchange_error_word() == 0
     y_ref, S_ref, cs_ref = O.prefill(inp, B, T, Hk, Hv, conv, norm)
     o = R.bits(run.o).reshape(B, T, Hv, D)
