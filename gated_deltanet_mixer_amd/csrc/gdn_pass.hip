@@ -47,6 +47,11 @@ static_assert(kRingP > 2 * kLagP + 1, "a mailbox slot must outlive the slowest s
 constexpr int kTB = 7 * 1024;       // bytes of T diag(beta) fragments and decay vectors (head of a tpf block)
 constexpr int kSDT = 6 * 1024;      // bytes per tile of Sb (4 fragments) and Delta (2 fragments)
 
+// (m & a) | (~m & b) on the bit patterns: a when m is all-ones, b when it is zero
+__device__ __forceinline__ float bit_select(unsigned int m, float a, float b) {
+    return __uint_as_float((m & __float_as_uint(a)) | (~m & __float_as_uint(b)));
+}
+
 struct PassArgs {
     const _Float16 *qkf, *tpf;
     const uint16_t *v, *z, *conv_w, *norm_w, *conv_state_in;
@@ -97,7 +102,18 @@ __device__ __forceinline__ void state_chunk(const unsigned char *smem, floatx4 (
     const _Float16 *sVc = reinterpret_cast<const _Float16 *>(smem + L::sV) + (c & 1) * L::BV * P64;
     half8 *sd = reinterpret_cast<half8 *>(const_cast<unsigned char *>(smem) + L::sSD + (c & 1) * NT * kSDT) + lane;
 
-    // K S over the four 32-key steps; S before the chunk goes to LDS for the read-out wave
+    // With one tile there are registers to spare: T diag(beta) of the chunk is then requested
+    // first, so that its LDS latency hides behind the K S products (with two tiles the extra
+    // 24 registers would spill)
+    const float4 *dec = reinterpret_cast<const float4 *>(tb + 6 * 1024);  // e^G [64], e^{G_C - G} [64], e^{G_C}
+    half8 tbf[6];
+    if constexpr (NT == 1) {
+#pragma unroll
+        for (int f = 0; f < 6; ++f) tbf[f] = *reinterpret_cast<const half8 *>(tb + f * 1024 + lane * 16);
+    }
+    // K S over the four 32-key steps.  The LDS stores of the chunk (S before the chunk and
+    // Delta, for the read-out wave) all come after the chunk's last LDS read: LDS operations
+    // complete in order, so a read issued after a store would wait for that store too.
     floatx4 ks[4][NT];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
@@ -110,17 +126,13 @@ __device__ __forceinline__ void state_chunk(const unsigned char *smem, floatx4 (
         for (int I = 0; I < 4; ++I) a[I] = *reinterpret_cast<const half8 *>(kb + (4 * I + s2) * 1024);
         half8 sb[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            sb[t] = pack_tiles(S[t][2 * s2], S[t][2 * s2 + 1]);
-            sd[t * (kSDT / 16) + 64 * s2] = sb[t];
-        }
+        for (int t = 0; t < NT; ++t) sb[t] = pack_tiles(S[t][2 * s2], S[t][2 * s2 + 1]);
 #pragma unroll
         for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int t = 0; t < NT; ++t) ks[I][t] = mfma16x16x32(a[I], sb[t], ks[I][t]);
     }
     // X = V - e^G K S
-    const float4 *dec = reinterpret_cast<const float4 *>(tb + 6 * 1024);  // e^G [64], e^{G_C - G} [64], e^{G_C}
     half8 Xb[NT][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -138,9 +150,15 @@ __device__ __forceinline__ void state_chunk(const unsigned char *smem, floatx4 (
         Xb[t][1] = pack_tiles(X[2], X[3]);
     }
     // Delta = T diag(beta) X (lower triangular: rows 0..31 use the first 32 tokens only)
-    half8 tbf[6];
+    if constexpr (NT != 1) {
 #pragma unroll
-    for (int f = 0; f < 6; ++f) tbf[f] = *reinterpret_cast<const half8 *>(tb + f * 1024 + lane * 16);
+        for (int f = 0; f < 6; ++f) tbf[f] = *reinterpret_cast<const half8 *>(tb + f * 1024 + lane * 16);
+    }
+    // e^{G_C - G} and e^{G_C}: the chunk's last LDS reads
+    float4 egc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) egc[u] = dec[16 + 4 * u + lq];
+    const float dC = reinterpret_cast<const float *>(tb + 6 * 1024)[2 * kC];
     half8 Dsb[NT][2];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -156,21 +174,33 @@ __device__ __forceinline__ void state_chunk(const unsigned char *smem, floatx4 (
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             sd[t * (kSDT / 16) + 64 * (4 + s)] = pack_tiles(d[2 * s], d[2 * s + 1]);
-            const float4 c0 = dec[16 + 8 * s + lq], c1 = dec[16 + 8 * s + 4 + lq];
+            const float4 c0 = egc[2 * s], c1 = egc[2 * s + 1];
             Dsb[t][s] = half8{(_Float16)(d[2 * s][0] * c0.x), (_Float16)(d[2 * s][1] * c0.y),
                               (_Float16)(d[2 * s][2] * c0.z), (_Float16)(d[2 * s][3] * c0.w),
                               (_Float16)(d[2 * s + 1][0] * c1.x), (_Float16)(d[2 * s + 1][1] * c1.y),
                               (_Float16)(d[2 * s + 1][2] * c1.z), (_Float16)(d[2 * s + 1][3] * c1.w)};
         }
     }
-    const float dC = reinterpret_cast<const float *>(tb + 6 * 1024)[2 * kC];
-    // S = e^{G_C} S + K^T Delta~, each k^T fragment used for every tile, then reloaded
+    // (S is packed afresh here: keeping the K S loop's packed copy alive until now would
+    // cost 8 NT registers, so the compiler is kept from reusing it)
 #pragma unroll
-    for (int ti = 0; ti < 8; ++ti) {
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            asm volatile("" : "+v"(S[t][2 * s2]), "+v"(S[t][2 * s2 + 1]));
+            sd[t * (kSDT / 16) + 64 * s2] = pack_tiles(S[t][2 * s2], S[t][2 * s2 + 1]);
+        }
+    // S = e^{G_C} S + K^T Delta~, each k^T fragment used for every tile, then reloaded.  The
+    // token step is the outer loop, so 8 NT independent accumulations separate the two
+    // products into one accumulator.
+#pragma unroll
+    for (int ti = 0; ti < 8; ++ti)
 #pragma unroll
         for (int t = 0; t < NT; ++t) S[t][ti] = S[t][ti] * dC;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int ti = 0; ti < 8; ++ti) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) S[t][ti] = mfma16x16x32(fkT[2 * ti + s], Dsb[t][s], S[t][ti]);
             fkT[2 * ti + s] = ld_frag(rnext, lane * 16, 2 * ti + s);
@@ -434,14 +464,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
                 wait_vmcnt<0>();
             }
-            // conv lane: rows rg * RPI .. +RPI-1, channels 4 c4 .. 4 c4 + 3 of the slice.  The
-            // conv runs on helpers 0, 3, 4, 5 (conv slots 0..3), never on the DMA helpers: the
-            // compiler makes every LDS read wait for the DMAs a wave has in flight.
-            const int cslot = hidx == 0 ? 0 : hidx - 2;
+            // conv lane: rows rg * RPI .. +RPI-1, channels 4 c4 .. 4 c4 + 3 of the slice.  Conv
+            // slots 0..3 sit on helpers 3, 4, 5, 0 (a one-tile slice needs two, which leaves the
+            // exchange helper free of conv), never on the DMA helpers: the compiler makes every
+            // LDS read wait for the DMAs a wave has in flight.
+            const int cslot = hidx == 0 ? 3 : hidx - 3;
             const int ci = (hidx == 0 || hidx >= 3) && cslot < NCV ? cslot * 64 + lane : -1;
             const int c4 = (ci >= 0 ? ci : 0) % NC4, rg = (ci >= 0 ? ci : 0) / NC4;
             float hwc[16];
             float nw[8];
+            // all-ones when the conv / the gated norm is on; opaque to the compiler, which would
+            // otherwise turn the selects below back into branches around the transcendentals
+            unsigned int conv_mask = a.conv ? ~0u : 0u, norm_mask = a.norm ? ~0u : 0u;
+            asm volatile("" : "+v"(conv_mask), "+v"(norm_mask));
             auto conv_v = [&](int cc) __attribute__((always_inline)) {
                 if (ci < 0) return;
                 const uint16_t *raw = sRawV + (cc % 3) * kC * BV;
@@ -472,13 +507,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     float u[RPI];
 #pragma unroll
                     for (int i = 0; i < RPI; ++i) {
-                        if (a.conv) {
-                            const float acc = hwc[4 * e] * x[i][e] + hwc[4 * e + 1] * x[i + 1][e] +
-                                              hwc[4 * e + 2] * x[i + 2][e] + hwc[4 * e + 3] * x[i + 3][e];
-                            u[i] = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc * -1.4426950408889634f));
-                        } else {
-                            u[i] = x[i + 3][e];
-                        }
+                        // computed either way and selected: a branch here would split the unrolled
+                        // loop into blocks the scheduler cannot interleave
+                        const float acc = hwc[4 * e] * x[i][e] + hwc[4 * e + 1] * x[i + 1][e] +
+                                          hwc[4 * e + 2] * x[i + 2][e] + hwc[4 * e + 3] * x[i + 3][e];
+                        const float sil = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc * -1.4426950408889634f));
+                        u[i] = bit_select(conv_mask, sil, x[i + 3][e]);
                     }
                     *reinterpret_cast<halfx2 *>(dst + e * P64) = halfx2{static_cast<_Float16>(u[0]), static_cast<_Float16>(u[1])};
                 }
@@ -562,16 +596,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             } else {
                 // ---------------------------------------------- conv (if any) and gating + store
                 const int gl = (hidx - (6 - NGT)) * 64 + lane;  // gating lane 0 .. 64 NGT - 1
-                const bool gater = hidx >= 6 - NGT;
+                static_assert(NGT == 3, "helpers 3, 4, 5 all gate");
                 int cg8[GPL];
 #pragma unroll
                 for (int u = 0; u < GPL; ++u) cg8[u] = ((gl + 64 * NGT * u) % NCG);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) nw[e] = 0.0f;
-                if (gater) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) nw[e] = sNW[cg8[0] * 8 + e];  // GPL items share the column group
-                }
+                for (int e = 0; e < 8; ++e) nw[e] = sNW[cg8[0] * 8 + e];  // GPL items share the column group
                 // z rows of chunk oc for this lane's items, through a buffer resource over the chunk's
                 // rows (rows past T read as zero).  Loads and stores are unconditional and in a fixed
                 // order (the next chunk's z is requested before this chunk's stores), for the same
@@ -597,9 +629,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 };
                 auto step = [&](int c, uint4(&zcur)[GPL], uint4(&znext)[GPL]) __attribute__((always_inline)) {
                     const int oc = c - 3 - kLagP;
-                    if (gater) z_load(oc + 1, znext);
+                    z_load(oc + 1, znext);
                     if (c + 1 < nch) conv_v(c + 1);
-                    if (gater) {
+                    {
                         const int ocl = max(oc, 0);
                         const float *src = sO + (ocl % kORingP) * VT;
                         const float *rs = sRstd + (ocl & 1) * kC;
@@ -610,15 +642,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                             float y[8];
 #pragma unroll
                             for (int e = 0; e < 8; ++e) y[e] = src[(cg8[u] * 8 + e) * PL + row];
-                            if (a.norm) {
-                                float zf[8];
-                                unpack_bf16x8(zcur[u], zf);
-                                const float rstd = rs[row];
+                            // the gated norm is computed either way and selected (no branch in the
+                            // unrolled loop; without the norm z is the readable v and rstd unused)
+                            float zf[8];
+                            unpack_bf16x8(zcur[u], zf);
+                            const float rstd = rs[row];
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) {
-                                    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(zf[e] * -1.4426950408889634f));
-                                    y[e] = nw[e] * (y[e] * rstd) * (zf[e] * sg);
-                                }
+                            for (int e = 0; e < 8; ++e) {
+                                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(zf[e] * -1.4426950408889634f));
+                                const float yn = nw[e] * (y[e] * rstd) * (zf[e] * sg);
+                                y[e] = bit_select(norm_mask, yn, y[e]);
                             }
                             const uint4 pk = pack_bf16x8(y);
                             __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{pk.x, pk.y, pk.z, pk.w}, ro, voff[u], 0, 0);
@@ -627,7 +660,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     lds_barrier();
                 };
                 uint4 zA[GPL], zB[GPL];
-                if (gater) z_load(-3 - kLagP, zA);
+                z_load(-3 - kLagP, zA);
                 int c = 0;
                 for (; c + 1 <= last; c += 2) {
                     step(c, zA, zB);
