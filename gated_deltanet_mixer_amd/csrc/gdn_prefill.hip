@@ -86,11 +86,8 @@ struct PrepLds {
     static constexpr size_t sL = 0;                        // fp32 [64][PL]    (per value head from here on)
     static constexpr size_t sTd = sL + 4 * kC * PL;        // fp32 [4][16][PTD]
     static constexpr size_t sT16T = sTd + 4 * 4 * 16 * PTD;  // fp16 [64][P64]  T transposed
-    static constexpr size_t sPst = sT16T + 2 * kC * P64;   // fp16 [10][256]  P staging
-    static constexpr size_t sTbst = sPst + 2 * 10 * kBlk;  // fp16 [10][256]  T diag(beta) staging
-    static constexpr size_t sG = sTbst + 2 * 10 * kBlk;    // fp32 [64]
-    static constexpr size_t sB = sG + 4 * kC;              // fp32 [64]
-    static constexpr size_t sGr = sB + 4 * kC;             // fp32 [r][64] g, then [r][64] beta, of every value head
+    static constexpr size_t sTbst = sT16T + 2 * kC * P64;  // fp16 [10][256]  T diag(beta) staging
+    static constexpr size_t sGr = sTbst + 2 * 10 * kBlk;   // fp32 [r][64] g (then G), then [r][64] beta, of every value head
     static_assert(sGr >= sK + 2 * kC * P128, "g/beta staging must not overlay q^/k^");
     static size_t bytes(int r) { return sGr + 2 * 4 * (size_t)kC * r; }
 };
@@ -104,10 +101,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     float *sL = reinterpret_cast<float *>(smem + PrepLds::sL);
     float *sTd = reinterpret_cast<float *>(smem + PrepLds::sTd);
     _Float16 *sT16T = reinterpret_cast<_Float16 *>(smem + PrepLds::sT16T);
-    _Float16 *sPst = reinterpret_cast<_Float16 *>(smem + PrepLds::sPst);
     _Float16 *sTbst = reinterpret_cast<_Float16 *>(smem + PrepLds::sTbst);
-    float *sG = reinterpret_cast<float *>(smem + PrepLds::sG);
-    float *sB = reinterpret_cast<float *>(smem + PrepLds::sB);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave bases stay scalar
@@ -297,24 +291,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
     }
 
-    // ---- 2. raw K K^T and Q K^T lower tiles, kept in registers (5 tasks per wave)
-    floatx4 raw[5];
+    // ---- 2. cumulative log-decays of every value head (wave w takes heads w, w + 4, ...) and
+    //         their decay vectors to the workspace; then the raw K K^T tiles of L and the
+    //         K Q^T tiles of P, kept in registers
+    for (int hr = wave; hr < a.r; hr += 4) {
+        const __amdgpu_buffer_rsrc_t rtp = make_rsrc(a.tpf + ((size_t)gc * a.Hv + kh * a.r + hr) * kTPF, kTPF * 2);
+        float gv = sGr[hr * kC + lane];
 #pragma unroll
-    for (int u = 0; u < 5; ++u) {
-        const int task = wave + 4 * u;
-        const bool isP = task >= 10;
-        const int tt = isP ? task - 10 : task;
-        int ti, tj;
-        tri_block(tt, ti, tj);
-        const _Float16 *Aop = isP ? sQ : sK;
+        for (int o = 1; o < 64; o <<= 1) {
+            const float t2 = __shfl_up(gv, o, 64);
+            if (lane >= o) gv += t2;
+        }
+        const float gC = __shfl(gv, 63, 64);
+        sGr[hr * kC + lane] = gv;
+        st_ws<false>(rtp, kVecOff * 2 + 4 * lane, hw_exp(gv));
+        st_ws<false>(rtp, kVecOff * 2 + 4 * (kC + lane), hw_exp(gC - gv));
+        if (lane < 4) st_ws<false>(rtp, kVecOff * 2 + 4 * (2 * kC + lane), hw_exp(gC));
+    }
+    // L tiles: task tt = wave + 4 u (u = 0..2, tt < 10), lower 16x16 blocks (ti, tj) of K K^T with
+    // the accumulator lane holding column j = 16 tj + l16, rows 16 ti + 4 lq + e.
+    // P fragments: operand fragment f of P (row block fI, token step fks) is built from the
+    // K Q^T tiles (fI, 2 fks) and (fI, 2 fks + 1): with K as the A operand and Q as the B operand
+    // the accumulator lane holds query row i = 16 fI + l16 at keys j = 16 J + 4 lq + e, which is
+    // the fragment's own lane layout, so P needs no staging.  Tiles above the diagonal are zero.
+    // Wave w owns fragments kPF[w] (6 fragments, 10 nonzero tiles over the four waves).
+    constexpr int kPF[4][2] = {{1, 0}, {3, 2}, {4, -1}, {5, -1}};
+    constexpr int kFI[6] = {0, 1, 2, 2, 3, 3}, kFKS[6] = {0, 0, 0, 1, 0, 1};
+    auto tile = [&](const _Float16 *Aop, int ai, const _Float16 *Bop, int bj) __attribute__((always_inline)) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const half8 av = lds_half8(Aop + (16 * ti + l16) * P128 + 32 * ks + 8 * lq);
-            const half8 bv = lds_half8(sK + (16 * tj + l16) * P128 + 32 * ks + 8 * lq);
+            const half8 av = lds_half8(Aop + (16 * ai + l16) * P128 + 32 * ks + 8 * lq);
+            const half8 bv = lds_half8(Bop + (16 * bj + l16) * P128 + 32 * ks + 8 * lq);
             acc = mfma16x16x32(av, bv, acc);
         }
-        raw[u] = acc;
+        return acc;
+    };
+    floatx4 rawL[3], rawP[2][2];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int tt = wave + 4 * u;
+        rawL[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (tt < 10) {
+            int ti, tj;
+            tri_block(tt, ti, tj);
+            rawL[u] = tile(sK, ti, sK, tj);
+        }
+    }
+#pragma unroll
+    for (int pf = 0; pf < 2; ++pf) {
+        const int f = kPF[wave][pf];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            rawP[pf][hh] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (f >= 0 && 2 * kFKS[f] + hh <= kFI[f]) rawP[pf][hh] = tile(sK, 2 * kFKS[f] + hh, sQ, kFI[f]);
+        }
     }
     lds_barrier();
 
@@ -322,43 +353,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     for (int hr = 0; hr < a.r; ++hr) {
         const int h = kh * a.r + hr;
         const __amdgpu_buffer_rsrc_t rtp = make_rsrc(a.tpf + ((size_t)gc * a.Hv + h) * kTPF, kTPF * 2);
-        if (wave == 0) {
-            float gv = sGr[hr * kC + lane];
-            const float bv = sGr[(a.r + hr) * kC + lane];
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const float t2 = __shfl_up(gv, o, 64);
-                if (lane >= o) gv += t2;
-            }
-            const float gc = __shfl(gv, 63, 64);
-            sG[lane] = gv;
-            sB[lane] = bv;
-            st_ws<false>(rtp, kVecOff * 2 + 4 * lane, hw_exp(gv));
-            st_ws<false>(rtp, kVecOff * 2 + 4 * (kC + lane), hw_exp(gc - gv));
-            if (lane < 4) st_ws<false>(rtp, kVecOff * 2 + 4 * (2 * kC + lane), hw_exp(gc));
-        }
-        lds_barrier();
+        const float *sG = sGr + hr * kC;          // cumulative log-decay G
+        const float *sB = sGr + (a.r + hr) * kC;  // beta
 
-        // L (fp32, strictly lower) and P (fp16 staging, lower incl. diagonal)
+        // P = (Q K^T) o R (lower incl. the diagonal), straight from registers to the workspace
 #pragma unroll
-        for (int u = 0; u < 5; ++u) {
-            const int task = wave + 4 * u;
-            const bool isP = task >= 10;
-            const int tt = isP ? task - 10 : task;
+        for (int pf = 0; pf < 2; ++pf) {
+            const int f = kPF[wave][pf];
+            if (f < 0) continue;
+            const int i = 16 * kFI[f] + l16;
+            const float gi = sG[i];
+            half8 v;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int j0 = 16 * (2 * kFKS[f] + hh) + 4 * lq;
+                const float4 gj = *reinterpret_cast<const float4 *>(sG + j0);
+                const float gjs[4] = {gj.x, gj.y, gj.z, gj.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[4 * hh + e] = static_cast<_Float16>(j0 + e <= i ? rawP[pf][hh][e] * hw_exp(gi - gjs[e]) : 0.0f);
+            }
+            st_ws<false>(rtp, (kPOff + f * kFrag) * 2 + lane * 16, v);
+        }
+        // L (fp32, strictly lower), rows i = 16 ti + 4 lq + e, column j = 16 tj + l16
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int tt = wave + 4 * u;
+            if (tt >= 10) continue;
             int ti, tj;
             tri_block(tt, ti, tj);
-            const int col = 16 * tj + l16;
+            const int col = 16 * tj + l16, r0 = 16 * ti + 4 * lq;
             const float gcol = sG[col];
+            const float4 gr = *reinterpret_cast<const float4 *>(sG + r0);
+            const float4 br = *reinterpret_cast<const float4 *>(sB + r0);
+            const float grs[4] = {gr.x, gr.y, gr.z, gr.w}, brs[4] = {br.x, br.y, br.z, br.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * ti + 4 * lq + e;
-                const float rdec = hw_exp(sG[row] - gcol);
-                if (isP)
-                    sPst[tt * kBlk + (4 * lq + e) * 16 + l16] =
-                        static_cast<_Float16>(col <= row ? raw[u][e] * rdec : 0.0f);
-                else
-                    sL[row * PL + col] = col < row ? sB[row] * raw[u][e] * rdec : 0.0f;
-            }
+            for (int e = 0; e < 4; ++e)
+                sL[(r0 + e) * PL + col] = col < r0 + e ? brs[e] * rawL[u][e] * hw_exp(grs[e] - gcol) : 0.0f;
         }
         lds_barrier();
 
@@ -427,36 +458,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
         lds_barrier();
 
-        // T diag(beta) (fragments 0..5) and P (6..11) to the workspace
-        for (int idx = tid; idx < 12 * 64; idx += 256) {
+        // T diag(beta) to the workspace as fragments 0..5: row tiles 0 and 1 take the first token
+        // step only, row tiles 2 and 3 both
+        for (int idx = tid; idx < 6 * 64; idx += 256) {
             const int f = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
-            const int g = f < 6 ? f : f - 6;
-            int row, ks;
-            if (g < 2) {
-                row = 16 * g + fl;
-                ks = 0;
-            } else if (f < 6) {  // T diag(beta): rows 32..63 take both k-steps
-                row = 32 + 16 * ((g - 2) >> 1) + fl;
-                ks = (g - 2) & 1;
-            } else {              // P: row tiles 2, 3 take both k-steps
-                row = 16 * (2 + ((g - 2) >> 1)) + fl;
-                ks = (g - 2) & 1;
-            }
-            const _Float16 *stg = f < 6 ? sTbst : sPst;
+            const int row = f < 2 ? 16 * f + fl : 32 + 16 * ((f - 2) >> 1) + fl;
+            const int ks = f < 2 ? 0 : (f - 2) & 1;
             const int bi = row >> 4;
             half8 v;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const int col = 32 * ks + 16 * hh + 4 * fq;  // 4 columns inside one 16-block
-                const int bj = col >> 4;
+                const int bj = 2 * ks + hh;  // the 16-column block of these 4 columns
                 half4 q4 = {0, 0, 0, 0};
-                if (bj <= bi) q4 = lds_half4(stg + (bi * (bi + 1) / 2 + bj) * kBlk + (row & 15) * 16 + (col & 15));
+                if (bj <= bi) q4 = lds_half4(sTbst + (bi * (bi + 1) / 2 + bj) * kBlk + (row & 15) * 16 + 4 * fq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }
-            st_ws<false>(rtp, ((f < 6 ? 0 : kPOff - 6 * kFrag) + idx * 8) * 2, v);
+            st_ws<false>(rtp, idx * 16, v);
         }
-        lds_barrier();
+        // (no barrier: the next head writes T staging only after its own first barrier, which
+        // every wave reaches after finishing these reads)
     }
 }
 
