@@ -3,16 +3,23 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu-baseline]
 
 One step = one gdn_prefill call over the whole batch of the headline workload
-(the Qwen3.5-0.8B-shaped layer, B=1, T=4096, 16 key / 16 value heads: conv,
-L2 norm, gated delta rule, gated RMSNorm), inputs already resident in HBM.
-Prints ONE JSON line.  `value` is prefill tokens/s of the layer.  Extra fields
-carry the roofline of the timed call, the decode step on the 27B-shaped
-B=256 workload (state GB/s, % of HBM) and the same batch checking two tokens per
-sequence with snapshots, the other prefill shapes, the 4B-shaped
-layer's tokens as 16 packed sequences of mixed lengths, one GPU's share of the
-27B-shaped layer under 16-way key-head sharding (the two-level scan beside the
-plain sequential pass), and the fp64
-CPU oracle timed on this host (a reported baseline, not a target).
+(default: the Qwen3.8-27B-shaped layer, B=1, T=262,144, 16 key / 48 value heads:
+conv, L2 norm, gated delta rule over 4,096 chunks, gated RMSNorm), inputs already
+resident in HBM.  Prints ONE JSON line.  `value` is prefill tokens/s of the layer;
+mean, median and min per call are reported, and the workspace error word of every
+input set is checked after the timed loop (a nonzero word fails the run).  The
+roofline object carries the achieved algorithmic HBM bandwidth of the call, the
+counter-measured HBM traffic and issued MFMA work of the same call (from the
+committed counter summary, while the kernel sources still hash to the value it
+records), and the useful-FLOP fraction of MFMA peak.  `detail` carries the other
+prefill shapes (the 0.8B- and 4B-shaped layers, the tiny T=64 case in
+microseconds), the decode step on the 27B-shaped B=256 batch (state GB/s, % of
+HBM) and the same batch checking two tokens per sequence, the 4B-shaped layer's
+tokens as 16 packed sequences, one GPU's share of the 27B-shaped layer under
+16-way key-head sharding (two-level scan beside the plain sequential pass), and
+the gate-logit entry point.  `cpu_baseline` is the fp64 CPU oracle timed on this
+host on a bounded sample of the headline workload (a reported baseline, not a
+target).
 
 Inputs are synthetic and seeded (torch's generator on the GPU for the timed
 runs, gdn_inputs for the CPU baseline) with the distributions of the pages'
@@ -41,11 +48,14 @@ USEFUL_FLOP_PER_TOKEN_HEAD = 6 * D * D + 5 * C * D + C * C / 3
 
 WORKLOADS = {
     # name: (B, T, Hk, Hv)
+    "tiny_T64": (1, 64, 1, 1),  # no conv, no gated norm
     "qwen35_0p8b_prefill_T4096": (1, 4096, 16, 16),
     "qwen35_4b_prefill_B4_T16384": (4, 16384, 16, 32),
     "qwen38_27b_prefill_T262144": (1, 262144, 16, 48),
 }
 DECODE = ("qwen38_27b_decode_B256", (256, 16, 48))
+NO_CONV_NORM = {"tiny_T64"}
+HEADLINE = "qwen38_27b_prefill_T262144"
 # packed sequences: the 4B-shaped layer's 65536 tokens as 16 sequences of mixed lengths
 PACKED = ("qwen35_4b_prefill_packed_16seq_T65536", (16, 65536, 16, 32))
 
@@ -60,10 +70,13 @@ def packed_lengths(n, total, seed=3000):
     return lens.tolist()
 
 
-def prefill_bytes(B, T, Hk, Hv) -> int:
+def prefill_bytes(B, T, Hk, Hv, fused=True) -> int:
     """Algorithmic HBM bytes of one prefill: raw q,k; v, z, o; g, beta; final state;
-    conv weights and conv tail (zero initial state and conv state are not read)."""
+    conv weights and conv tail (zero initial state and conv state are not read).
+    Without conv and gated norm (the tiny case): no z, conv weights or conv tail."""
     Cc = 2 * Hk * D + Hv * D
+    if not fused:
+        return B * T * (2 * Hk * D * 2 + 2 * Hv * D * 2 + Hv * 8) + B * Hv * D * D * 4
     per_tok = 2 * Hk * D * 2 + 3 * Hv * D * 2 + Hv * 8
     return B * T * per_tok + B * Hv * D * D * 4 + Cc * 4 * 2 + B * 3 * Cc * 2 + D * 2
 
@@ -88,7 +101,7 @@ def _gen(torch, gen, shape, kind):
     raise ValueError(kind)
 
 
-def make_prefill_set(torch, gdn, B, T, Hk, Hv, seed):
+def make_prefill_set(torch, gdn, B, T, Hk, Hv, seed, conv=True, norm=True, segments=0):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
     Cc = 2 * Hk * D + Hv * D
@@ -105,7 +118,9 @@ def make_prefill_set(torch, gdn, B, T, Hk, Hv, seed):
     d["o"] = torch.empty((B, T, Hv, D), dtype=torch.bfloat16, device="cuda")
     d["state_out"] = torch.empty((B, Hv, D, D), dtype=torch.float32, device="cuda")
     d["conv_state_out"] = torch.empty((B, 3, Cc), dtype=torch.bfloat16, device="cuda")
-    shape = gdn.make_shape(B, T, Hk, Hv)
+    if not conv:  # no conv: the boundary takes no conv weights and returns no conv tail
+        d["conv_w"] = d["conv_state_out"] = None
+    shape = gdn.make_shape(B, T, Hk, Hv, conv=conv, norm=norm, segments=segments)
     nws = gdn.gdn_prefill_workspace_size(shape)
     d["ws"] = torch.zeros(nws, dtype=torch.uint8, device="cuda")
     d["shape"] = shape
@@ -134,44 +149,58 @@ def run_prefill_gate_logits(gdn, d):
 
 
 def time_calls(torch, fn, sets, steps, warmup):
-    """Average ms per call over `steps` calls (cycling the input sets), with
-    HIP events on the current stream, bracketed by device syncs."""
+    """Per-call times in ms over `steps` back-to-back calls (cycling the input sets), from
+    HIP events recorded on the current stream (the stream the library launches on) between
+    the calls, bracketed by device syncs.  Returns (mean, median, min, wall seconds)."""
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t_wall = time.perf_counter()
-    start.record()
+    ev[0].record()
     for i in range(steps):
         fn(sets[i % len(sets)])
-    end.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    return start.elapsed_time(end) / steps, t_wall
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mean = ev[0].elapsed_time(ev[steps]) / steps
+    return mean, per[len(per) // 2], per[0], t_wall
+
+
+def check_sets(gdn, sets):
+    """The workspace error word of every input set after the timed calls: a timed-out wait
+    between workgroups or a skipped packed sequence fails the run."""
+    for d in sets:
+        gdn.gdn_prefill_check(d["ws"])
 
 
 def bench_prefill(torch, gdn, name, steps, warmup, gate_logits=False):
     B, T, Hk, Hv = WORKLOADS[name]
+    fused = name not in NO_CONV_NORM
     per_set = prefill_bytes(B, T, Hk, Hv) + B * T * Hk * 2 * D * 2
     nsets = max(1, min(4, math.ceil(320e6 / per_set)))  # rotate past the 256 MB Infinity Cache
-    sets = [make_prefill_set(torch, gdn, B, T, Hk, Hv, seed=1000 + i) for i in range(nsets)]
+    sets = [make_prefill_set(torch, gdn, B, T, Hk, Hv, seed=1000 + i, conv=fused, norm=fused) for i in range(nsets)]
     if gate_logits:
         for i, d in enumerate(sets):
             add_gate_logits(torch, d, Hv, seed=2000 + i)
     torch.cuda.synchronize()
     run = run_prefill_gate_logits if gate_logits else run_prefill
-    ms, wall = time_calls(torch, lambda d: run(gdn, d), sets, steps, warmup)
-    nbytes = prefill_bytes(B, T, Hk, Hv)
+    ms, med, mn, wall = time_calls(torch, lambda d: run(gdn, d), sets, steps, warmup)
+    check_sets(gdn, sets)
+    nbytes = prefill_bytes(B, T, Hk, Hv, fused)
     flops = USEFUL_FLOP_PER_TOKEN_HEAD * B * T * Hv
     res = {
         "workload": name + (" (gdn_prefill_gate_logits)" if gate_logits else ""), "B": B, "T": T, "Hk": Hk,
-        "Hv": Hv, "ms_per_call": ms,
+        "Hv": Hv, "conv_and_norm": fused, "ms_per_call": ms, "ms_median": med, "ms_min": mn,
         "tokens_per_s": B * T / (ms * 1e-3), "algorithmic_bytes": nbytes,
         "hbm_GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / HBM_PEAK,
         "useful_TFLOPs": flops / (ms * 1e-3) / 1e12, "mfma_useful_frac": flops / (ms * 1e-3) / MFMA_FP16_PEAK,
         "roof_frac": max(nbytes / HBM_PEAK, flops / MFMA_FP16_PEAK) / (ms * 1e-3),
-        "input_sets": nsets, "steps": steps, "wall_s": wall,
+        "input_sets": nsets, "steps": steps, "wall_s": wall, "error_word": 0,
     }
+    if name in NO_CONV_NORM:
+        res["us_per_call"] = ms * 1e3
     del sets
     torch.cuda.empty_cache()
     return res
@@ -196,13 +225,15 @@ def bench_prefill_packed(torch, gdn, steps, warmup):
         gdn.gdn_prefill_packed(dd["shape"], dd["cu"], dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["z"],
                                dd["conv_w"], dd["norm_w"], None, None, dd["o"], dd["state_out"],
                                dd["conv_state_out"], dd["ws"])
-    ms, wall = time_calls(torch, run, [d], steps, warmup)
+    ms, med, mn, wall = time_calls(torch, run, [d], steps, warmup)
+    check_sets(gdn, [d])
     # per-token bytes as the even batch; one final state and conv tail per sequence
     nbytes = prefill_bytes(1, T, Hk, Hv) + (N - 1) * (Hv * D * D * 4 + 3 * Cc * 2)
     flops = USEFUL_FLOP_PER_TOKEN_HEAD * T * Hv
     res = {
         "workload": name + " (gdn_prefill_packed)", "sequences": N, "T_total": T, "Hk": Hk, "Hv": Hv,
-        "lengths_min_max": [min(lens), max(lens)], "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+        "lengths_min_max": [min(lens), max(lens)], "ms_per_call": ms, "ms_median": med, "ms_min": mn,
+        "tokens_per_s": T / (ms * 1e-3),
         "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
         "hbm_frac": nbytes / (ms * 1e-3) / HBM_PEAK, "useful_TFLOPs": flops / (ms * 1e-3) / 1e12,
         "mfma_useful_frac": flops / (ms * 1e-3) / MFMA_FP16_PEAK, "steps": steps, "wall_s": wall,
@@ -218,29 +249,20 @@ SHARD = ("qwen38_27b_prefill_T262144_keyhead_shard_1of16", (1, 262144, 1, 3))
 
 def bench_prefill_shard(torch, gdn, steps, warmup):
     """The few-heads, long-sequence shape the two-level scan is for, timed as the library
-    plans it (segments) and, for comparison, with the plain sequential pass
-    (GDN_PREFILL_SEGMENTS=0)."""
+    plans it (segments) and, for comparison, with the plain sequential pass forced through
+    the shape's prefill_segments field (1)."""
     name, (B, T, Hk, Hv) = SHARD
     out = {"workload": name, "B": B, "T": T, "Hk": Hk, "Hv": Hv}
-    old = os.environ.get("GDN_PREFILL_SEGMENTS")
-    try:
-        for leg, env in (("plain_sequential", "0"), ("planned", None)):
-            if env is None:
-                os.environ.pop("GDN_PREFILL_SEGMENTS", None)
-            else:
-                os.environ["GDN_PREFILL_SEGMENTS"] = env
-            d = make_prefill_set(torch, gdn, B, T, Hk, Hv, seed=1200)
-            torch.cuda.synchronize()
-            ms, _ = time_calls(torch, lambda dd: run_prefill(gdn, dd), [d], steps, warmup)
-            out[leg + "_ms_per_call"] = ms
-            out[leg + "_workspace_MiB"] = d["ws"].numel() / 2 ** 20
-            del d
-            torch.cuda.empty_cache()
-    finally:
-        if old is None:
-            os.environ.pop("GDN_PREFILL_SEGMENTS", None)
-        else:
-            os.environ["GDN_PREFILL_SEGMENTS"] = old
+    for leg, segments in (("plain_sequential", 1), ("planned", 0)):
+        d = make_prefill_set(torch, gdn, B, T, Hk, Hv, seed=1200, segments=segments)
+        torch.cuda.synchronize()
+        ms, med, mn, _ = time_calls(torch, lambda dd: run_prefill(gdn, dd), [d], steps, warmup)
+        check_sets(gdn, [d])
+        out[leg + "_ms_per_call"] = ms
+        out[leg + "_ms_min"] = mn
+        out[leg + "_workspace_MiB"] = d["ws"].numel() / 2 ** 20
+        del d
+        torch.cuda.empty_cache()
     ms = out["planned_ms_per_call"]
     nbytes = prefill_bytes(B, T, Hk, Hv)
     flops = USEFUL_FLOP_PER_TOKEN_HEAD * B * T * Hv
@@ -270,10 +292,11 @@ def bench_decode(torch, gdn, steps, warmup):
     def fn(dd):
         gdn.gdn_decode_step(shape, dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["z"], dd["conv_w"],
                             dd["norm_w"], dd["state"], dd["conv_state"], dd["o"])
-    ms, wall = time_calls(torch, fn, [d], steps, warmup)
+    ms, med, mn, wall = time_calls(torch, fn, [d], steps, warmup)
     nbytes = decode_bytes(B, Hk, Hv)
     state_bytes = 2 * B * Hv * D * D * 4
     res = {"workload": DECODE[0], "B": B, "Hk": Hk, "Hv": Hv, "us_per_step": ms * 1e3,
+           "us_median": med * 1e3, "us_min": mn * 1e3,
            "tokens_per_s": B / (ms * 1e-3), "algorithmic_bytes": nbytes,
            "hbm_GBps": nbytes / (ms * 1e-3) / 1e9, "hbm_frac": nbytes / (ms * 1e-3) / HBM_PEAK,
            "state_GBps": state_bytes / (ms * 1e-3) / 1e9, "steps": steps}
@@ -316,7 +339,7 @@ def bench_decode_multi(torch, gdn, steps, warmup, T=2):
         gdn.gdn_decode_multi(shape, dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["z"], dd["conv_w"],
                              dd["norm_w"], dd["state"], dd["conv_state"], dd["o"], dd["state_snaps"],
                              dd["conv_snaps"])
-    ms, wall = time_calls(torch, fn, [d], steps, warmup)
+    ms, med, mn, wall = time_calls(torch, fn, [d], steps, warmup)
     nbytes = decode_multi_bytes(B, T, Hk, Hv)
     res = {"workload": f"{DECODE[0]} checking T={T} tokens per sequence (gdn_decode_multi, snapshots)",
            "B": B, "T": T, "Hk": Hk, "Hv": Hv, "us_per_call": ms * 1e3, "tokens_per_s": B * T / (ms * 1e-3),
@@ -327,68 +350,84 @@ def bench_decode_multi(torch, gdn, steps, warmup, T=2):
     return res
 
 
-def cpu_baseline(name, budget_s=20.0, min_s=10.0):
-    """The fp64 oracle (as it stands) on this host's cores, on the headline
-    workload: all of its (sequence, value-head) chains, repeated until about
-    `min_s` seconds have passed, or as many whole chains as fit `budget_s` when
-    one full pass would take longer."""
-    import numpy as np
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, target_s=15.0, min_s=10.0):
+    """The fp64 oracle (as it stands) on this host's cores, on a bounded sample of the
+    headline workload: every (sequence, value-head) chain of the layer over its first Ts
+    tokens, Ts sized from a one-chain calibration so that one pass takes about `target_s`
+    seconds with all threads, repeated until `min_s` seconds have passed.  The recurrence
+    does the same work for every token, so chain-tokens per second over the sample is the
+    oracle's rate for the whole layer; the sample's inputs are drawn with the workload's
+    distributions under a seed tag of their own."""
     import gdn_inputs as GI
     from oracle import oracle as O
     w = GI.WORKLOADS[name]
-    inp = GI.make_inputs(w)
-    nchains = w.B * w.Hv
     threads = O.num_threads()
-    # calibrate on one chain
+    nchains = w.B * w.Hv
+    cal = GI.Workload(name + "_calibration", 1, min(1024, w.T), w.Hk, w.Hv, conv=w.conv, norm=w.norm, tag=w.tag + 200)
+    ci = GI.make_inputs(cal)
     t = time.perf_counter()
-    O.prefill(inp, w.B, w.T, w.Hk, w.Hv, w.conv, w.norm, chains=[0], threads=1, want_conv_state=False)
-    one = time.perf_counter() - t
-    per_round = max(1, min(threads, nchains))
-    full_est = one * math.ceil(nchains / per_round)
-    if full_est <= budget_s:
-        chains = np.arange(nchains)
-    else:
-        n = int(max(per_round, per_round * (budget_s // max(one, 1e-9))))
-        chains = np.arange(min(n, nchains))
+    O.prefill(ci, 1, cal.T, w.Hk, w.Hv, w.conv, w.norm, chains=[0], threads=1, want_conv_state=False)
+    per_chain_token = (time.perf_counter() - t) / cal.T
+    used = max(1, min(threads, nchains))
+    Ts = int(target_s * used / (nchains * per_chain_token))
+    Ts = max(64, min(w.T, Ts // 64 * 64))
+    sample = GI.Workload(name + "_sample", w.B, Ts, w.Hk, w.Hv, conv=w.conv, norm=w.norm, tag=w.tag + 100)
+    inp = GI.make_inputs(sample)
     reps, el = 0, 0.0
     t = time.perf_counter()
     while reps == 0 or (el < min_s and reps < 200):
-        O.prefill(inp, w.B, w.T, w.Hk, w.Hv, w.conv, w.norm, chains=chains, threads=threads,
-                  want_conv_state=False)
+        O.prefill(inp, w.B, Ts, w.Hk, w.Hv, w.conv, w.norm, threads=threads, want_conv_state=False)
         reps += 1
         el = time.perf_counter() - t
-    n = len(chains)
-    used = min(threads, n)
     # tokens/s of the layer = chain-tokens/s divided by the layer's Hv chains per token
-    return {"value": reps * n * w.T / el / w.Hv, "unit": "tokens/s", "cores": used, "kind": "oracle",
-            "sample": f"{n} of {nchains} (sequence, value-head) chains of {name}, all {w.T} tokens each, "
-                      f"{reps} pass(es); fp64 C oracle (conv, L2 norm, token-by-token recurrence, gated "
-                      f"RMSNorm) with OpenMP over chains; {el:.1f} s wall",
-            "host_cpus": os.cpu_count()}
+    return {"value": reps * nchains * Ts / el / w.Hv, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"all {nchains} (sequence, value-head) chains of {name} over their first {Ts} of {w.T} "
+                      f"tokens, {reps} pass(es), {el:.1f} s wall; fp64 C oracle (conv, L2 norm, token-by-token "
+                      f"recurrence, gated RMSNorm) with OpenMP over chains",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
 
 
-TRAFFIC_FILES = {"qwen35_0p8b_prefill_T4096": "profiles/prefill_qwen35_0p8b_T4096_hbm_traffic.txt"}
+# Counter summaries taken with rocprofv3 on one MI355X (profiles/), per headline workload.
+COUNTER_FILES = {"qwen38_27b_prefill_T262144": "profiles/prefill_qwen38_27b_T262144_counters.txt"}
 
 
-def measured_traffic(name):
-    """HBM bytes per call from the committed counter summary of this workload,
-    or None when there is none or the kernel sources changed since it was taken."""
+def measured_counters(name):
+    """Per-call figures of the committed counter summary of this workload (HBM traffic
+    from FETCH_SIZE / WRITE_SIZE scaled by the copy-probe factors, issued MFMA work and
+    MFMA-busy cycles), or None when there is none or the kernel sources changed since it
+    was taken."""
     import hashlib
-    rel = TRAFFIC_FILES.get(name)
+    rel = COUNTER_FILES.get(name)
     if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
         return None
     rec = {}
     for line in open(os.path.join(ROOT, rel)):
-        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_call", "sources_sha256", "sources"):
+        if ":" in line:
             k, v = line.split(":", 1)
-            rec[k] = v.strip()
+            rec[k.strip()] = v.strip()
     if not all(k in rec for k in ("traffic_bytes_per_call", "sources_sha256", "sources")):
         return None
     h = hashlib.sha256()
     for src in rec["sources"].split():
         with open(os.path.join(ROOT, src), "rb") as f:
             h.update(f.read())
-    return int(rec["traffic_bytes_per_call"]) if h.hexdigest() == rec["sources_sha256"] else None
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    out = {"traffic": int(rec["traffic_bytes_per_call"])}
+    for k in ("mfma_issued_flop_per_call", "mfma_busy_cycles_per_call", "calibration"):
+        if k in rec:
+            out[k] = rec[k] if k == "calibration" else float(rec[k])
+    return out
 
 
 def main(argv=None):
@@ -396,7 +435,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="qwen35_0p8b_prefill_T4096", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="skip decode and the other prefill shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -429,16 +468,34 @@ def main(argv=None):
         for name in WORKLOADS:
             if name != args.workload:
                 B, T, Hk, Hv = WORKLOADS[name]
-                steps = max(3, min(args.steps, int(2e8 // (B * T * Hv))))
+                steps = max(3, min(200, int(2e8 // (B * T * Hv))))
                 extra[name] = bench_prefill(torch, gdn, name, steps, 2)
         # few heads, long sequence: the two-level scan against the plain sequential pass
         extra[SHARD[0]] = bench_prefill_shard(torch, gdn, 5, 1)
         # the 4B-shaped layer's tokens as packed sequences of mixed lengths
         extra[PACKED[0]] = bench_prefill_packed(torch, gdn, 20, 2)
         # the same layer through the entry point that takes the gate logits
-        extra[args.workload + "_gate_logits"] = bench_prefill(torch, gdn, args.workload, max(20, args.steps // 4), 5,
+        extra[args.workload + "_gate_logits"] = bench_prefill(torch, gdn, args.workload, max(10, args.steps // 4), 3,
                                                               gate_logits=True)
     B, T, Hk, Hv = WORKLOADS[args.workload]
+    ctr = measured_counters(args.workload)
+    ms = head["ms_per_call"]
+    roof = {
+        "kernel": "one gdn_prefill call: chunk_prep_kernel then pass_kernel on the caller's stream, timed "
+                  "together with HIP events on that stream",
+        "bound": "hbm", "achieved": head["hbm_GBps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+        "frac": head["hbm_frac"], "traffic": ctr["traffic"] if ctr else None,
+        "algorithmic_bytes": head["algorithmic_bytes"],
+        "mfma_useful_TFLOPs": head["useful_TFLOPs"], "mfma_useful_frac": head["mfma_useful_frac"],
+    }
+    if ctr:
+        roof["traffic_over_algorithmic"] = ctr["traffic"] / head["algorithmic_bytes"]
+        if "mfma_issued_flop_per_call" in ctr:
+            roof["mfma_issued_TFLOPs"] = ctr["mfma_issued_flop_per_call"] / (ms * 1e-3) / 1e12
+            roof["mfma_issued_frac"] = ctr["mfma_issued_flop_per_call"] / (ms * 1e-3) / MFMA_FP16_PEAK
+        if "mfma_busy_cycles_per_call" in ctr:
+            roof["mfma_busy_cycles_per_call"] = ctr["mfma_busy_cycles_per_call"]
+        roof["counters"] = COUNTER_FILES[args.workload]
     out = {
         "metric": "GDN prefill tokens/s per layer (% MFMA peak); decode-step state GB/s (% HBM)",
         "value": head["tokens_per_s"],
@@ -446,20 +503,18 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["ms_per_call"],
+        "ms_per_step": ms,
+        "ms_median": head["ms_median"],
+        "ms_min": head["ms_min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 I/O, fp16 MFMA operands, fp32 accumulate and state",
+        "dtype": "f16 MFMA operands, f32 accumulate and state, bf16 I/O",
         "data": "synthetic, seeded (torch generator on the GPU), distributions of the pages' workloads",
         "config": {"workload": args.workload, "B": B, "T": T, "Hk": Hk, "Hv": Hv, "Dk": D, "Dv": D,
-                   "chunk": C, "conv_width": 4, "gated_norm": True, "parallelism": "single GPU"},
-        "roofline": {
-            "kernel": "one gdn_prefill call = chunk_prep_kernel + chain_kernel launches, timed together",
-            "bound": "hbm", "achieved": head["hbm_GBps"], "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-            "frac": head["hbm_frac"], "traffic": measured_traffic(args.workload),
-            "mfma_useful_TFLOPs": head["useful_TFLOPs"], "mfma_useful_frac": head["mfma_useful_frac"],
-        },
+                   "chunk": C, "conv_width": 0 if args.workload in NO_CONV_NORM else 4,
+                   "gated_norm": args.workload not in NO_CONV_NORM, "parallelism": "single GPU"},
+        "roofline": roof,
         "detail": {"headline": head, **extra},
     }
     if not args.no_cpu_baseline:
