@@ -395,18 +395,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAXT <
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sv[e] = alpha * sv[e] + kv * d4[e];
                 S[m] = sv;
+                // The whole offset goes in the vector offset and the scalar offset is the constant
+                // 0: the compiler then models the hazard of a VALU write to the data registers of
+                // a wide store right behind it (it does not for a register scalar offset), and
+                // inserts the wait state itself.
                 if (keep)
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sv), rdst, toff,
-                                                           hr * kHeadBytes + m * 16 * kD * 4, kStateStorePolicy);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sv), rdst,
+                                                           toff + hr * kHeadBytes + m * 16 * kD * 4, 0,
+                                                           kStateStorePolicy);
             }
-            // The stores' data registers stay untouched until all eight are issued: after the
-            // last token the state is otherwise dead, and the compiler would reuse one register
-            // quad for every store, rewriting it with VALU results right behind each store (no
-            // wait state is modelled for buffer stores with a scalar offset).  That gave wrong
-            // final states here, so the values are kept alive past the stores.
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int m = 0; m < kRows; ++m) asm volatile("" ::"v"(S[m]));
 
             if (tid < kD) {
                 const int j = tid;
