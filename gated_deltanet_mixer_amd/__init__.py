@@ -79,11 +79,12 @@ _lib.gdn_decode_multi.argtypes = [_sp] + [_vp] * 14
 _lib.gdn_decode_multi_gate_logits.argtypes = [_sp] + [_vp] * 16
 _lib.gdn_prefill_packed_gate_logits.argtypes = [_sp] + [_vp] * 17 + [C.c_size_t, _vp]
 _lib.gdn_prefill_check.argtypes = [_vp, C.c_size_t, _vp]
+_lib.gdn_prefill_no_workspace.argtypes = [_sp] + [_vp] * 13 + [_vp]
 
 EXPORTED = ("gdn_state_init", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step",
             "gdn_prefill_gate_logits", "gdn_decode_step_gate_logits", "gdn_prefill_packed",
             "gdn_prefill_packed_gate_logits", "gdn_decode_multi", "gdn_decode_multi_gate_logits",
-            "gdn_prefill_check", "gdn_status_string", "gdn_last_error")
+            "gdn_prefill_check", "gdn_prefill_no_workspace", "gdn_status_string", "gdn_last_error")
 
 
 def _ptr(t):
@@ -134,6 +135,19 @@ def gdn_prefill(shape: gdn_shape, q, k, v, g, beta, z, conv_w, norm_w, state_in,
                           _ptr(state_out), _ptr(conv_state_out), _ptr(workspace), int(workspace_bytes),
                           _stream(stream))
     _check("gdn_prefill", rc)
+
+
+GDN_STATIC_SCRATCH_BYTES = 128 << 20
+
+
+def gdn_prefill_no_workspace(shape: gdn_shape, q, k, v, g, beta, z, conv_w, norm_w, state_in, conv_state_in,
+                             o, state_out, conv_state_out, stream=None) -> None:
+    """gdn_prefill on the library's static per-GPU scratch (no workspace, no allocation;
+    shapes up to GDN_STATIC_SCRATCH_BYTES of workspace; calls on one GPU must not overlap)."""
+    rc = _lib.gdn_prefill_no_workspace(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(z),
+                                       _ptr(conv_w), _ptr(norm_w), _ptr(state_in), _ptr(conv_state_in), _ptr(o),
+                                       _ptr(state_out), _ptr(conv_state_out), _stream(stream))
+    _check("gdn_prefill_no_workspace", rc)
 
 
 def gdn_prefill_check(workspace, workspace_bytes: int | None = None, stream=None) -> None:

@@ -3,6 +3,7 @@
 // Every check runs on the host before the first HIP call, so a rejected call
 // enqueues nothing and needs no device.
 #include <stdint.h>
+#include <mutex>
 #include <string.h>
 
 #include "gdn.h"
@@ -104,16 +105,52 @@ int gdn_prefill_check(const void *workspace, size_t workspace_bytes, void *strea
 
 namespace {
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of gdn_prefill_no_workspace: a file-scope device array of
+// kStaticScratchBytes that every GPU the library runs on holds until the process ends.
+// In host code `scratch` is only a stand-in for the symbol; the array's address on a
+// device comes from hipGetSymbolAddress, looked up once per device with that device
+// current, and that address is what the kernels get.  Every call on a GPU shares the
+// array; the prep kernel clears the part that must start at zero on every call.
+constexpr size_t kStaticScratchBytes = GDN_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, or nullptr (with the reason recorded) when
+// it cannot be had.
+void *static_scratch_address() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail("hipGetDevice", e), nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return fail("gdn_prefill_no_workspace: device index out of range"), nullptr;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail("hipGetSymbolAddress(scratch)", e), nullptr;
+        if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255)) return fail("hipGetSymbolAddress(scratch): unaligned"), nullptr;
+        g_scratch_addr[dev] = ptr;
+    }
+    return g_scratch_addr[dev];
+}
+
 // g, beta are the gate logits a, b when A_log and dt_bias are given (both or neither);
 // cu_seqlens is given exactly when the shape carries GDN_PACKED.
 int prefill_impl(const gdn_shape *s, const int32_t *cu_seqlens, const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                  const float *beta, const float *A_log, const float *dt_bias, const uint16_t *z,
                  const uint16_t *conv_w, const uint16_t *norm_w, const float *state_in,
                  const uint16_t *conv_state_in, uint16_t *o, float *state_out, uint16_t *conv_state_out,
-                 void *workspace, size_t workspace_bytes, void *stream) {
+                 void *workspace, size_t workspace_bytes, void *stream, bool static_scratch = false) {
     int rc = check_shape(s, true);
     if (rc) return rc;
     const bool packed = (s->flags & GDN_PACKED) != 0;
+    // The static scratch is the library's own array: it is neither null nor misaligned nor
+    // shared with any caller buffer, and its address is only looked up once every host check
+    // has passed.  Here it stands in as a placeholder for those checks.
+    alignas(256) static const unsigned char placeholder[256] = {};
+    if (static_scratch) workspace = const_cast<unsigned char *>(placeholder), workspace_bytes = kStaticScratchBytes;
     if (packed != (cu_seqlens != nullptr)) return GDN_EINVAL;
     if (cu_seqlens && !aligned(cu_seqlens, 4)) return GDN_EINVAL;
     if ((A_log == nullptr) != (dt_bias == nullptr)) return GDN_EINVAL;
@@ -140,22 +177,24 @@ int prefill_impl(const gdn_shape *s, const int32_t *cu_seqlens, const uint16_t *
     } inputs[] = {{q, nqk}, {k, nqk}, {v, nv}, {g, ngb}, {beta, ngb}, {norm ? z : nullptr, nv},
                   {conv_w, nw}, {norm_w, nn}, {state_in, nst}, {conv_state_in, ncs},
                   {A_log, Hv * 4}, {dt_bias, Hv * 4}, {cu_seqlens, (B + 1) * 4}};
+    const size_t wsb = static_scratch ? 0 : workspace_bytes;  // overlap() ignores empty ranges
     for (const auto &in : inputs)
-        if (overlap(o, nv, in.p, in.n) || overlap(workspace, workspace_bytes, in.p, in.n)) return GDN_EINVAL;
+        if (overlap(o, nv, in.p, in.n) || overlap(workspace, wsb, in.p, in.n)) return GDN_EINVAL;
     if (overlap(conv_state_out, ncs, conv_state_in, ncs)) return GDN_EINVAL;
     // state_out may be state_in exactly, but must not partly overlap anything else
     if (state_out != state_in && overlap(state_out, nst, state_in, nst)) return GDN_EINVAL;
     for (const auto &in : inputs)
         if (in.p != state_in && overlap(state_out, nst, in.p, in.n)) return GDN_EINVAL;
     if (overlap(o, nv, state_out, nst) || overlap(o, nv, conv_state_out, ncs) ||
-        overlap(workspace, workspace_bytes, o, nv) || overlap(workspace, workspace_bytes, state_out, nst) ||
-        overlap(workspace, workspace_bytes, conv_state_out, ncs) || overlap(state_out, nst, conv_state_out, ncs))
+        overlap(workspace, wsb, o, nv) || overlap(workspace, wsb, state_out, nst) ||
+        overlap(workspace, wsb, conv_state_out, ncs) || overlap(state_out, nst, conv_state_out, ncs))
         return GDN_EINVAL;
 
     PrefillPlan plan;
     plan_prefill(s->B, s->T, s->Hk, s->Hv, packed, s->prefill_segments, &plan);
     if (plan.nslots * s->Hk > 0x7fffffffLL) return GDN_EINVAL;
     if (workspace_bytes < plan.total_bytes) return GDN_EWORKSPACE;
+    if (static_scratch && !(workspace = static_scratch_address())) return GDN_EHIP;
 
     PrefillParams p;
     p.q = q; p.k = k; p.v = v; p.z = norm ? z : nullptr; p.conv_w = conv_w; p.norm_w = norm ? norm_w : nullptr;
@@ -233,6 +272,14 @@ int gdn_prefill(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const 
                 uint16_t *conv_state_out, void *workspace, size_t workspace_bytes, void *stream) {
     return prefill_impl(s, nullptr, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state_in, conv_state_in,
                         o, state_out, conv_state_out, workspace, workspace_bytes, stream);
+}
+
+int gdn_prefill_no_workspace(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                             const float *g, const float *beta, const uint16_t *z, const uint16_t *conv_w,
+                             const uint16_t *norm_w, const float *state_in, const uint16_t *conv_state_in,
+                             uint16_t *o, float *state_out, uint16_t *conv_state_out, void *stream) {
+    return prefill_impl(s, nullptr, q, k, v, g, beta, nullptr, nullptr, z, conv_w, norm_w, state_in, conv_state_in,
+                        o, state_out, conv_state_out, nullptr, 0, stream, true);
 }
 
 int gdn_prefill_gate_logits(const gdn_shape *s, const uint16_t *q, const uint16_t *k, const uint16_t *v,

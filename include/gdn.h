@@ -162,6 +162,33 @@ int gdn_prefill(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
 int gdn_prefill_check(const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine): its workspace is a file-scope device array
+ * of the library, GDN_STATIC_SCRATCH_BYTES (128 MiB) on every GPU the library
+ * runs on, held until the process ends.  Its address on a device is looked up
+ * once, on the first call with that device current, after the host checks.
+ *
+ * Arguments, layouts, results and errors are those of gdn_prefill (even
+ * batches only).  A shape whose gdn_prefill_workspace_size exceeds
+ * GDN_STATIC_SCRATCH_BYTES is rejected with GDN_EWORKSPACE before any HIP
+ * call (the 0.8B-shaped layer, 16/16 heads, fits up to T = 8192 tokens).
+ * Every call on one GPU uses the same array, which keeps the last call's
+ * contents; each call clears what must start at zero.  Calls that overlap in
+ * time on one GPU (several streams, several host threads) race on the array
+ * and give wrong results: serialise them.  Its error word cannot be read with
+ * gdn_prefill_check (the caller holds no workspace pointer); a timed-out wait
+ * shows as NaN rows, as for gdn_prefill.
+ */
+#define GDN_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdn_prefill_no_workspace(const gdn_shape *shape, const uint16_t *q, const uint16_t *k,
+                             const uint16_t *v, const float *g, const float *beta, const uint16_t *z,
+                             const uint16_t *conv_w, const uint16_t *norm_w, const float *state_in,
+                             const uint16_t *conv_state_in, uint16_t *o, float *state_out,
+                             uint16_t *conv_state_out, void *stream);
+
+/*
  * One decode step: one new token per sequence, updating the recurrent state
  * and the conv window in place ("How Qwen3.5 works" §13.3: each linear layer
  * shifts its conv state and takes one recurrent step; the state is

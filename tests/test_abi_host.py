@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(
         ["gdn_decode_step", "gdn_decode_step_gate_logits", "gdn_last_error", "gdn_prefill",
          "gdn_prefill_gate_logits", "gdn_prefill_packed", "gdn_prefill_packed_gate_logits",
-         "gdn_decode_multi", "gdn_decode_multi_gate_logits", "gdn_prefill_check",
+         "gdn_decode_multi", "gdn_decode_multi_gate_logits", "gdn_prefill_check", "gdn_prefill_no_workspace",
          "gdn_prefill_workspace_size", "gdn_state_init", "gdn_status_string"])
 
 
