@@ -295,6 +295,10 @@ int gdn_decode_multi_gate_logits(const gdn_shape *shape, const uint16_t *q, cons
  *                 call does not synchronise; a sequence whose bounds break this
  *                 rule is skipped (nothing of it is read or written, its outputs
  *                 keep their contents) and every other sequence is still computed.
+ *                 Offsets that decrease anywhere (cu_seqlens[b] > cu_seqlens[b+1]
+ *                 for some b) cannot be placed at all: then every sequence is
+ *                 skipped.  Either case sets the error bit gdn_prefill_check reports
+ *                 as GDN_ESKIPPED.
  *  q, k           [T][Hk][128] bf16 (token-major over the packed batch)
  *  v, z, o        [T][Hv][128] bf16
  *  g, beta        [T][Hv] fp32

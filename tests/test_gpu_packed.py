@@ -154,6 +154,26 @@ def test_packed_sequence_with_bad_bounds_is_skipped():
     _check_against_oracle(run, tok, state, conv_state, cu, Hk, Hv, True, True, "bad bounds", skip=(1,))
 
 
+def test_packed_with_decreasing_offsets_skips_everything():
+    """Offsets that decrease somewhere cannot be placed: every sequence is skipped, nothing is
+    written, and the error word says so."""
+    R = _R()
+    lengths, Hk, Hv = [70, 20, 90], 1, 2
+    tok, state, conv_state, cu, T = _batch(lengths, Hk, Hv, True, True, tag=1335)
+    cu = cu.copy()
+    cu[1], cu[2] = cu[2], cu[1]  # [0, 90, 70, 180]: sequence 1 runs backwards
+    print(f"[packed] decreasing offsets cu={cu.tolist()}", flush=True)
+    run = R.PackedPrefill(tok, cu, T, Hk, Hv, True, True, state_in=state, conv_state_in=conv_state)
+    run.state_out.fill_(7.0)
+    run.conv_state_out.fill_(7)
+    run.o.fill_(7)
+    run.run()
+    torch.cuda.synchronize()
+    assert run.exchange_error_word() == 2
+    assert bool((run.state_out == 7.0).all()) and bool((run.conv_state_out == 7).all())
+    assert bool((run.o == 7).all())
+
+
 def test_packed_from_zero_states():
     """No initial states (NULL state_in and conv_state_in): every sequence starts from zeros."""
     R = _R()
