@@ -24,10 +24,10 @@
 //           kernel stores both orientations), T diag(beta) and the decays from LDS.
 //   wave 1  read-out: q^ fragments, P and e^G straight from the workspace a chunk ahead;
 //           S and Delta of the chunk from the state wave through LDS.
-//   waves 2..7 helpers: the k^, T diag(beta) / decay and raw-v DMA into LDS rings, conv +
-//           SiLU of v, the per-row sums of squares the gated norm needs from every slice
-//           of a head (tagged words in a workspace mailbox, bounded waits), and the
-//           gated RMSNorm with the bf16 store.
+//   waves 2..7 helpers: helper 0 the per-row sums of squares the gated norm needs from
+//           every slice of a head (tagged words in a workspace mailbox, bounded waits);
+//           helper 1 the DMA of the k^ fragments, T diag(beta) / decays and raw v rows into
+//           LDS rings; helpers 2..5 conv + SiLU of v and the gated RMSNorm with the bf16 store.
 // One LDS barrier per iteration hands data between the roles; every hand-off is at least
 // one barrier away.  Work items (head, slice) come from eight ticket queues, one per XCD,
 // grouped by key head so that the slices reading one key head's operands share an L2.
@@ -275,13 +275,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NCV = NCONV / 64;          // conv helpers
     // gating items: one row piece of 8 columns per lane and iteration, on helpers 6 - NGT .. 5
     constexpr int NGATE = kC * NCG;          // 128 or 256
-    constexpr int NGT = 3;                   // gating helpers
+    constexpr int NGT = 4;                   // gating helpers
     constexpr int GPL = (NGATE + 64 * NGT - 1) / (64 * NGT);  // items per gating lane (1 or 2)
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hidx = wave - 2;  // helper index (0..5) for waves 2..7
+    // Helper index (0..5) of waves 2..7.  A workgroup's waves go to the four SIMDs in turn, so
+    // waves 4 and 5 share a SIMD with the state and the read-out wave: they take the two light
+    // roles (DMA, exchange), and the four conv + gating helpers get SIMDs 2 and 3 to themselves.
+    const int hidx = wave == 4 ? 1 : wave == 5 ? 0 : wave < 4 ? wave : wave - 2;
     float *sO = reinterpret_cast<float *>(smem + L::sO);
     uint16_t *sRawV = reinterpret_cast<uint16_t *>(smem + L::sRawV);
     uint16_t *sHalo = reinterpret_cast<uint16_t *>(smem + L::sHalo);
@@ -422,26 +425,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                           h * kD + sv0 + cg * 8);
                 *reinterpret_cast<uint4 *>(sHalo + r3 * BV + cg * 8) = rw;
             }
-            // DMA groups: k^ fragments and T diag(beta) + decays of chunk cc -> ring slot cc % 3;
-            // raw v rows of chunk cc -> ring slot cc % 3.  Chunks past the last repeat the last
-            // (a harmless duplicate), so that every iteration issues the same loads.  Helper 1
-            // issues k^ fragments 0..13, helper 2 the rest.
-            const bool dma1 = hidx == 1, dma2 = hidx == 2;
+            // DMA group of chunk cc (helper 1 alone): its k^ fragments and T diag(beta) + decays
+            // -> ring slot cc % 3, and (rows_dma) its raw v rows -> ring slot cc % 3.  Chunks past
+            // the last repeat the last (a harmless duplicate), so that every iteration issues the
+            // same loads.
+            const bool dma1 = hidx == 1;
             auto dma_ops = [&](int cc) __attribute__((always_inline)) {
                 const int cl = min(cc, nch - 1);
                 unsigned char *kslot = smem + L::sK + (cc % 3) * 16384;
                 const _Float16 *kb = qk0 + (size_t)cl * qk_stride + kKOff;
-                if (dma1) {
 #pragma unroll
-                    for (int f = 0; f < 14; ++f) dma16(kb + f * kFrag + lane * 8, kslot + f * 1024);
-                } else {
+                for (int f = 0; f < 16; ++f) dma16(kb + f * kFrag + lane * 8, kslot + f * 1024);
+                unsigned char *tslot = smem + L::sTB + (cc % 3) * kTB;
+                const unsigned char *tb = reinterpret_cast<const unsigned char *>(tp0 + (size_t)cl * tp_stride);
 #pragma unroll
-                    for (int f = 14; f < 16; ++f) dma16(kb + f * kFrag + lane * 8, kslot + f * 1024);
-                    unsigned char *tslot = smem + L::sTB + (cc % 3) * kTB;
-                    const unsigned char *tb = reinterpret_cast<const unsigned char *>(tp0 + (size_t)cl * tp_stride);
-#pragma unroll
-                    for (int f = 0; f < 7; ++f) dma16(tb + f * 1024 + lane * 16, tslot + f * 1024);
-                }
+                for (int f = 0; f < 7; ++f) dma16(tb + f * 1024 + lane * 16, tslot + f * 1024);
             };
             auto rows_dma = [&](int cc) __attribute__((always_inline)) {
                 const int c0 = min(cc, nch - 1) * kC;
@@ -454,22 +452,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     dma16b(rr, ((row * a.Hv + h) * kD + sv0 + 8 * cg) * 2, dst + u * 512);
                 }
             };
-            if (dma1 || dma2) {
+            if (dma1) {
                 dma_ops(0);
                 dma_ops(1);
-                if (dma2) {
-                    rows_dma(0);
-                    rows_dma(1);
-                    rows_dma(2);
-                }
+                rows_dma(0);
+                rows_dma(1);
+                rows_dma(2);
                 wait_vmcnt<0>();
             }
             // conv lane: rows rg * RPI .. +RPI-1, channels 4 c4 .. 4 c4 + 3 of the slice.  Conv
-            // slots 0..3 sit on helpers 3, 4, 5, 0 (a one-tile slice needs two, which leaves the
-            // exchange helper free of conv), never on the DMA helpers: the compiler makes every
-            // LDS read wait for the DMAs a wave has in flight.
-            const int cslot = hidx == 0 ? 3 : hidx - 3;
-            const int ci = (hidx == 0 || hidx >= 3) && cslot < NCV ? cslot * 64 + lane : -1;
+            // slots 0..3 sit on helpers 2..5 (a one-tile slice needs two), never on the DMA
+            // helper: the compiler makes every LDS read wait for the DMAs a wave has in flight.
+            const int cslot = hidx - 2;
+            const int ci = hidx >= 2 && cslot < NCV ? cslot * 64 + lane : -1;
             const int c4 = (ci >= 0 ? ci : 0) % NC4, rg = (ci >= 0 ? ci : 0) / NC4;
             float hwc[16];
             float nw[8];
@@ -543,7 +538,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                 __attribute__((always_inline)) {
                     const int rc = c - 2 - kLagP;
                     mb_request(rc + 1, mnext);
-                    if (c + 1 < nch) conv_v(c + 1);
                     // 1/rms of chunk rc from every slice's words (a word without the chunk's tag is waited for)
                     if (a.norm && rc >= 0 && rc < nch) {
                         float tot = 0.0f;
@@ -578,17 +572,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     step(c + 1, mB, mA);
                 }
                 if (c <= last) step(c, mA, mB);
-            } else if (dma1 || dma2) {
+            } else if (dma1) {
                 // ---------------------------------------------- DMA only
                 for (int c = 0; c <= last; ++c) {
                     __builtin_amdgcn_sched_barrier(0);
                     dma_ops(c + 2);
-                    if (dma2) rows_dma(c + 3);
+                    rows_dma(c + 3);
                     // the previous iteration's group has landed
-                    if (dma1)
-                        wait_vmcnt<14>();
-                    else
-                        wait_vmcnt<9 + NRD>();
+                    wait_vmcnt<16 + 7 + NRD>();
                     __builtin_amdgcn_s_barrier();
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
                 }
@@ -596,7 +587,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             } else {
                 // ---------------------------------------------- conv (if any) and gating + store
                 const int gl = (hidx - (6 - NGT)) * 64 + lane;  // gating lane 0 .. 64 NGT - 1
-                static_assert(NGT == 3, "helpers 3, 4, 5 all gate");
+                static_assert(NGT == 4, "helpers 2, 3, 4, 5 all gate");
                 int cg8[GPL];
 #pragma unroll
                 for (int u = 0; u < GPL; ++u) cg8[u] = ((gl + 64 * NGT * u) % NCG);
