@@ -1,6 +1,7 @@
 """Benchmark of the Gated DeltaNet mixer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu-baseline]
+                    [--copy-probe] [--decode-only]
 
 One step = one gdn_prefill call over the whole batch of the headline workload
 (default: the Qwen3.8-27B-shaped layer, B=1, T=262,144, 16 key / 48 value heads:
@@ -437,6 +438,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--no-extra", action="store_true", help="skip decode and the other prefill shapes")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the 27B-shaped B=256 decode step and print its record (for counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy three times (calibrates HBM byte counters)")
@@ -460,6 +463,9 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decode(torch, gdn, args.steps, args.warmup)}), flush=True)
+        return 0
     head = bench_prefill(torch, gdn, args.workload, args.steps, args.warmup)
     extra = {}
     if not args.no_extra:
