@@ -41,7 +41,7 @@ struct PrefillPlan {
     int nchunks;         // ceil(T / 64)
     long long nslots;    // chunk operand slots: B nchunks, or floor(T / 64) + B for packed sequences
     size_t xch_bytes;    // exchange area: 256-byte header (error word, queue tickets, exit count),
-                         // tagged per-row partial sums of every (sequence, value head), counters
+                         // then the tagged per-row partial sums of every (sequence, value head)
     size_t mbox_bytes;   // the tagged partial sums inside the exchange area
     size_t qk_bytes;     // per (slot, key head): q^, k^, k^T fragments (fp16)
     size_t tp_bytes;     // per (slot, value head): T diag(beta), P (lower blocks, fp16), decay vectors
@@ -57,7 +57,6 @@ struct PrefillRegions {
     unsigned int *tickets;   // [8] work-queue tickets
     unsigned int *exits;     // workgroups that left the two-level scan's first pass
     unsigned long long *mbox;
-    unsigned int *counters;  // [B Hv]
     _Float16 *qkf, *tpf;
     unsigned char *seg;      // two-level scan regions (read-outs, segment maps, start states)
 };

@@ -41,9 +41,8 @@ namespace gdn {
 namespace {
 
 constexpr int kLagP = 2;            // iterations between publishing a chunk's row sums and reading the siblings'
-constexpr int kRingP = 8;           // mailbox slots per slice
 constexpr int kORingP = kLagP + 3;  // pre-norm output tiles held in LDS
-static_assert(kRingP > 2 * kLagP + 1, "a mailbox slot must outlive the slowest sibling's read");
+static_assert(kMboxRing > 2 * kLagP + 1, "a mailbox slot must outlive the slowest sibling's read");
 constexpr int kTB = 7 * 1024;       // bytes of T diag(beta) fragments and decay vectors (head of a tpf block)
 constexpr int kSDT = 6 * 1024;      // bytes per tile of Sb (4 fragments) and Delta (2 fragments)
 
@@ -58,7 +57,7 @@ struct PassArgs {
     const float *state_in;
     uint16_t *o, *conv_state_out;
     float *state_out;
-    unsigned long long *mbox;  // [B Hv][8 slices][kRingP][64]: tagged per-row partial sums of squares
+    unsigned long long *mbox;  // [B Hv][8 slices][kMboxRing][64]: tagged per-row partial sums of squares
     unsigned int *err;         // error word (bit 0: a bounded wait timed out; bit 1: a packed sequence skipped)
     unsigned int *tickets;     // [8] next item of each XCD queue
     const int *cu;             // packed sequences: [B + 1] token offsets (nullptr: even batch)
@@ -524,14 +523,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // store here is issued unconditionally and in a fixed order, and the sibling words
                 // for the next iteration are requested before this iteration's publish: waiting for
                 // them then never waits for a store.  Two register sets alternate between iterations.
-                unsigned long long *mrow = a.mbox + (size_t)chain * kTiles * kRingP * kC + lane;  // row = lane
-                unsigned long long *trash = a.mbox + (size_t)a.B * a.Hv * kTiles * kRingP * kC + lane;
+                unsigned long long *mrow = a.mbox + (size_t)chain * kTiles * kMboxRing * kC + lane;  // row = lane
+                unsigned long long *trash = a.mbox + (size_t)a.B * a.Hv * kTiles * kMboxRing * kC + lane;
                 unsigned long long mA[NSL], mB[NSL];
                 auto mb_request = [&](int cc, unsigned long long(&m)[NSL]) __attribute__((always_inline)) {
                     const int ccl = min(max(cc, 0), nch - 1);
 #pragma unroll
                     for (int sib = 0; sib < NSL; ++sib)
-                        m[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRingP + (ccl % kRingP)) * kC, __ATOMIC_RELAXED,
+                        m[sib] = __hip_atomic_load(mrow + ((size_t)sib * kMboxRing + (ccl % kMboxRing)) * kC, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
                 };
                 auto step = [&](int c, unsigned long long(&mcur)[NSL], unsigned long long(&mnext)[NSL])
@@ -545,7 +544,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         for (int sib = 0; sib < NSL; ++sib) {
                             unsigned long long w = mcur[sib];
                             if ((uint32_t)(w >> 32) != (uint32_t)(rc + 1))
-                                w = spin_load(mrow + ((size_t)sib * kRingP + (rc % kRingP)) * kC, (uint32_t)(rc + 1), a.err,
+                                w = spin_load(mrow + ((size_t)sib * kMboxRing + (rc % kMboxRing)) * kC, (uint32_t)(rc + 1), a.err,
                                               broken);
                             tot += __uint_as_float((uint32_t)w);
                         }
@@ -560,7 +559,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     float ss = 0.0f;
 #pragma unroll
                     for (int j = 0; j < BV; ++j) ss += src[j * PL] * src[j * PL];
-                    __hip_atomic_store(pub ? mrow + ((size_t)s * kRingP + ((c - 2) % kRingP)) * kC : trash,
+                    __hip_atomic_store(pub ? mrow + ((size_t)s * kMboxRing + ((c - 2) % kMboxRing)) * kC : trash,
                                        ((unsigned long long)(uint32_t)(c - 1) << 32) | __float_as_uint(ss),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     lds_barrier();

@@ -12,43 +12,30 @@
 //   S'    = e^{G_C} S + K^T diag(e^{G_C - G_j}) Delta
 // followed by the gated RMSNorm of each output row (model spec node gdn.norm).
 //
-// Kernels.
-//  chunk_prep_kernel  one workgroup per (sequence, chunk, key head), all in
-//                     parallel.  conv + SiLU + L2 norm (+ 1/sqrt(128) on q) of
-//                     the chunk's q/k rows -> fp16 q^, k^; Q K^T and K K^T
-//                     once per key head; then for each of its r value heads
-//                     the decays, T = (I + L)^{-1} (16x16 diagonal blocks by
-//                     substitution in fp32, the rest as block products on
-//                     MFMA), T diag(beta) and P = (Q K^T) o R.  Everything
-//                     that does not depend on the state is done here, once,
-//                     instead of inside the sequential loop of every value
-//                     slice.  Its outputs are written as MFMA operand
-//                     fragments (64 lanes x 16 bytes each), so the sequential
-//                     pass loads every operand straight into registers with
-//                     one coalesced 1 KB load per fragment.
-//  chain_kernel<NT>   one workgroup (4 waves, one per SIMD) per (sequence,
-//                     value head, slice of 16*NT value columns); state columns
-//                     evolve independently, so a head splits into 8/NT slices
-//                     on different CUs.  Waves 0..NT-1 each own one 16-column
-//                     tile of the state in MFMA accumulator registers and run
-//                     the chunk loop -- the only sequential dependency.  The
-//                     accumulator layout of two adjacent 16-row tiles is the
-//                     B-operand layout of a 16x16x32 MFMA under one fixed
-//                     permutation of k, applied to the A operands as well, so
-//                     no shuffle sits in the loop.  Each fragment register set
-//                     is reloaded with the next chunk's data right after its
-//                     last use, a full chunk ahead of its next use.  The other
-//                     waves load raw v and z, convert v (conv + SiLU) for the
-//                     next chunk, and finish the gated RMSNorm of an earlier
-//                     chunk; one LDS barrier per chunk hands tiles between
-//                     the roles.  The norm needs all 128 columns of a row:
-//                     every 16-column tile publishes per-row sums of squares
-//                     as tagged 64-bit words (value | chunk tag) and each
-//                     slice reads its siblings' words kLag chunks later.
-//                     Slices are handed out from per-XCD ticket queues in the
-//                     order workgroups start, so a slice only ever waits for
-//                     siblings that are running or next in line; every wait
-//                     is bounded.
+// Kernels (all on the caller's stream, one after the other).
+//  chunk_prep_kernel    one workgroup per (sequence, chunk, key head), all in
+//                       parallel.  conv + SiLU + L2 norm (+ 1/sqrt(128) on q) of
+//                       the chunk's q/k rows -> fp16 q^, k^ (and k^T); Q K^T and
+//                       K K^T once per key head; then for each of its r value heads
+//                       the decays, T = (I + L)^{-1} (16x16 diagonal blocks by
+//                       substitution in fp32, the rest as block products on
+//                       MFMA), T diag(beta) and P = (Q K^T) o R.  Everything
+//                       that does not depend on the state is done here, once,
+//                       instead of inside the sequential loop of every value
+//                       slice.  Its outputs are written as MFMA operand
+//                       fragments (64 lanes x 16 bytes each), so the later
+//                       kernels load every operand straight into registers (or
+//                       LDS) with one coalesced 1 KB load per fragment.  It also
+//                       clears the workspace's exchange area.
+//  pass_kernel<NT>      (gdn_pass.hip) the sequential pass over the chunks of every
+//                       (sequence, value head), with the read-out and the gated
+//                       RMSNorm.
+//  Two-level scan, for few heads and long sequences (in place of pass_kernel):
+//  segment_pass_kernel  every segment of a sequence on its own, from the identity
+//                       and from zero (the segment map is affine in its start state);
+//  seg_combine_kernel   the start state of every segment and the final state;
+//  seg_output_kernel    the outputs from the segments' read-outs and start states,
+//                       with the gated RMSNorm.
 // All contractions use fp16 MFMA operands with fp32 accumulation; the state is
 // carried in fp32 across chunks; inputs and outputs are bf16.
 #include <algorithm>
@@ -273,7 +260,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const int ff = f & 15;
             const _Float16 *src = M + (16 * (ff >> 2) + fl) * P128 + 32 * (ff & 3) + 4 * fq;
             const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
-            st_ws<false>(rq, idx * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            st_ws(rq, idx * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         }
         // k^T fragment 32 + 2 ti + s2, lane fl + 16 fq: key 16 ti + fl at tokens
         // 32 s2 + 4 fq + e and 32 s2 + 16 + 4 fq + e (e = 0..3)
@@ -287,7 +274,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 v[e] = src[e * P128];
                 v[4 + e] = src[(16 + e) * P128];
             }
-            st_ws<false>(rq, (32 * 64 + idx) * 16, v);
+            st_ws(rq, (32 * 64 + idx) * 16, v);
         }
     }
 
@@ -304,9 +291,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
         const float gC = __shfl(gv, 63, 64);
         sGr[hr * kC + lane] = gv;
-        st_ws<false>(rtp, kVecOff * 2 + 4 * lane, hw_exp(gv));
-        st_ws<false>(rtp, kVecOff * 2 + 4 * (kC + lane), hw_exp(gC - gv));
-        if (lane < 4) st_ws<false>(rtp, kVecOff * 2 + 4 * (2 * kC + lane), hw_exp(gC));
+        st_ws(rtp, kVecOff * 2 + 4 * lane, hw_exp(gv));
+        st_ws(rtp, kVecOff * 2 + 4 * (kC + lane), hw_exp(gC - gv));
+        if (lane < 4) st_ws(rtp, kVecOff * 2 + 4 * (2 * kC + lane), hw_exp(gC));
     }
     // L tiles: task tt = wave + 4 u (u = 0..2, tt < 10), lower 16x16 blocks (ti, tj) of K K^T with
     // the accumulator lane holding column j = 16 tj + l16, rows 16 ti + 4 lq + e.
@@ -373,7 +360,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 for (int e = 0; e < 4; ++e)
                     v[4 * hh + e] = static_cast<_Float16>(j0 + e <= i ? rawP[pf][hh][e] * hw_exp(gi - gjs[e]) : 0.0f);
             }
-            st_ws<false>(rtp, (kPOff + f * kFrag) * 2 + lane * 16, v);
+            st_ws(rtp, (kPOff + f * kFrag) * 2 + lane * 16, v);
         }
         // L (fp32, strictly lower), rows i = 16 ti + 4 lq + e, column j = 16 tj + l16
 #pragma unroll
@@ -474,7 +461,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }
-            st_ws<false>(rtp, idx * 16, v);
+            st_ws(rtp, idx * 16, v);
         }
         // (no barrier: the next head writes T staging only after its own first barrier, which
         // every wave reaches after finishing these reads)
@@ -482,72 +469,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 }
 
 // ========================================================================
-// chain_kernel<NT>
+// segment_pass_kernel: the first pass of the two-level scan
 // ========================================================================
+//
+// Every segment of seg_chunks chunks runs on its own, with 256 virtual value columns per
+// head: columns 0..127 start from the identity and carry no values (their state ends as
+// the segment's transition M, their read-out as R, so that R S_start is what the start
+// state adds to the outputs), columns 128..255 start from zero with the real values
+// (state N, read-out O0).  A segment's outputs are then O0 + R S_start and its final state
+// M S_start + N (the segment map is affine in the start state), which the two later
+// kernels apply.  One workgroup of 8 waves per (sequence, value head, segment, slice of
+// 32 virtual columns).  Pipeline of one iteration c (every role runs iterations
+// 0..nch+2+kSegLag with one LDS barrier each; the lags keep every hand-off one barrier or
+// more away):
+//   A (state, waves 0, 1)     chunk c: X, Delta, S update; Sb(c), Db(c) -> LDS
+//   B (read-out, waves 2, 3)  chunk c-1: O = e^G Q S + P Delta -> sO
+//   L (load, wave 5)          DMA of the k^ fragments of chunk c+2 and the raw v of chunk
+//                             c+3; a DMA issued in iteration c is complete at the barrier
+//                             that ends iteration c+1, so its data is used from c+2 on
+//   V (helpers, waves 4, 6, 7) conv + SiLU of v for chunk c+1; the read-out of chunk
+//                             c-3-kSegLag to the workspace in fp16
+constexpr int kSegLag = 3;
+constexpr int kORing = kSegLag + 3;  // read-out tiles in LDS
+constexpr int kSegNT = 2;            // 16-column tiles per workgroup
+constexpr int kOpSlot = 16 * 1024;   // operand slot: the chunk's k^ fragments
+constexpr int kSD = 6 * 1024;        // per tile: Sb (4 fragments) and Db (2 fragments)
 
-// Pipeline of one iteration c of the chain workgroup (every role runs iterations
-// 0..nch+2+kLag with one LDS barrier each; the lags keep every hand-off one
-// barrier or more away):
-//   A (state)  chunk c:     X, Delta, S update; Sb(c), Db(c) -> LDS
-//   B (output) chunk c-1:   O = e^G Q S + P Delta -> sO
-//   L (loads)  DMA of the operands of chunk c+2, raw v of chunk c+3 and z of chunk
-//              c-1-kLag; a DMA issued in iteration c is complete at the barrier that
-//              ends iteration c+1, so its data is used from iteration c+2 on
-//   V (VALU)   conv + SiLU of v for chunk c+1; gated RMSNorm and store of chunk
-//              c-3-kLag; the first V wave also publishes the row sums of chunk
-//              c-2 and finishes 1/rms of chunk c-2-kLag from the siblings' sums
-constexpr int kLag = 3;
-constexpr int kRing = 8;           // mailbox slots: chunks c-2-kLag .. c+kLag-2 can be live
-constexpr int kORing = kLag + 3;   // pre-norm output tiles in LDS
-// How far ahead the load wave works is set per tile count (ChainLds::D): a DMA issued in
-// iteration j is waited for at the end of iteration j + D - 1 and used from j + D + 1 on.
-static_assert(kRing >= 2 * kLag + 1, "mailbox depth");
-
-struct ChainArgs {
+struct SegPassArgs {
     const _Float16 *qkf, *tpf;
-    const uint16_t *v, *z, *conv_w, *norm_w, *conv_state_in;
-    const float *state_in;
-    uint16_t *o, *conv_state_out;
-    float *state_out;
-    unsigned long long *mbox;  // [B*Hv][kTiles][kRing][64]: per-row sums of squares of each slice
-    unsigned int *counters;    // [B*Hv]
-    unsigned int *err;
+    const uint16_t *v, *conv_w, *conv_state_in;
+    uint16_t *conv_state_out;
     unsigned int *tickets;     // [8] next item of each XCD queue
     unsigned int *exits;       // workgroups that have left the item loop
-    const unsigned int *ready; // [slots][Hk] prep stamps
-    unsigned int stamp;
-    int check;                 // the prep kernel may still be running: follow the stamps
-    const int *cu;             // packed sequences: [B + 1] token offsets (nullptr: even batch)
-    // segment pass (two-level scan): segments of seg_chunks chunks, nseg per sequence
     _Float16 *seg_out;         // per (chunk slot, value head) kSegBlk halves: R as MFMA A fragments, O0 rows
     float *seg_state;          // [B Hv nseg][128][256] fp32: final [M | N] of each segment
     int nseg, seg_chunks;
-    int B, T, Hk, Hv, r, Cc, conv, norm, nch, n_items, grid;
-    float eps_norm;
+    int B, T, Hk, Hv, r, Cc, conv, nch, n_items, grid;
 };
-
-constexpr int kOpSlot = 16 * 1024;         // operand slot: the chunk's k^ fragments
-constexpr int kSD = 6 * 1024;              // per tile: Sb (4 fragments) and Db (2 fragments)
 
 template <int NT>
 struct ChainLds {
     static constexpr int BV = 16 * NT;
     static constexpr int VT = BV * PL;                          // floats of one column-major [BV][64] tile
-    // DMA lead in iterations: 2 where the LDS has room for the extra slots (one 16-column
-    // tile), else 1.  The operand, raw-v and z rings hold D + 2 chunks each.
-    static constexpr int D = NT == 1 ? 2 : 1;
-    static constexpr int NSLOT = D + 2;
+    static constexpr int NSLOT = 3;                              // ring depth of the DMA'd operands and raw v
     static constexpr size_t sOp = 0;                             // [NSLOT][kOpSlot]     DMA'd operands
     static constexpr size_t sSD = sOp + (size_t)NSLOT * kOpSlot; // [2][NT][kSD]         Sb, Db fragments per tile
     static constexpr size_t sV = sSD + 2 * NT * kSD;             // fp16 [2][BV][P64]     conv(v) of the slice
-    static constexpr size_t sO = sV + 2 * 2 * BV * P64;          // fp32 [kORing][BV][PL] pre-norm output
+    static constexpr size_t sO = sV + 2 * 2 * BV * P64;          // fp32 [kORing][BV][PL] read-out
     static constexpr size_t sRawV = sO + 4 * kORing * VT;        // bf16 [NSLOT][64][BV]  raw v
-    static constexpr size_t sZ = sRawV + 2 * NSLOT * kC * BV;    // bf16 [NSLOT][64][BV]  z
-    static constexpr size_t sHalo = sZ + 2 * NSLOT * kC * BV;    // bf16 [2][3][BV]       raw v rows before a chunk
-    static constexpr size_t sRstd = sHalo + 2 * 2 * 3 * BV;      // fp32 [2][64]          gated-norm 1/rms
-    static constexpr size_t sCW = sRstd + 4 * 2 * kC;            // fp32 [BV][4]          conv taps of the v channels
-    static constexpr size_t sNW = sCW + 4 * 4 * BV;              // fp32 [BV]             gated-norm weights
-    static constexpr size_t bytes = sNW + 4 * BV;
+    static constexpr size_t sHalo = sRawV + 2 * NSLOT * kC * BV; // bf16 [2][3][BV]       raw v rows before a chunk
+    static constexpr size_t sCW = sHalo + 2 * 2 * 3 * BV;        // fp32 [BV][4]          conv taps of the v channels
+    static constexpr size_t bytes = sCW + 4 * 4 * BV;
     static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
@@ -719,98 +691,41 @@ __device__ __forceinline__ void out_step(unsigned char *smem, const OutFrags &fr
 constexpr int kSegR = 16 * kFrag;
 constexpr int kSegBlk = kSegR + kC * kD;
 
-
-// The prep kernel may still be running while this one starts: prep block
-// (operand slot gc, key head kh) stores this call's stamp once its operands
-// are written back (agent-scope release).  A chunk's operands are first touched
-// after its stamp has been seen, and no cache of this kernel holds lines of them
-// from before (caches are invalidated when a kernel starts and nothing loads a
-// chunk early), so a relaxed load of the stamp suffices.
-__device__ __forceinline__ const unsigned int *ready_word(const ChainArgs &a, int gc, int kh) {
-    return a.ready + (size_t)gc * a.Hk + kh;
-}
-__device__ __forceinline__ bool stamp_ok(const ChainArgs &a, unsigned int w) { return (int)(w - a.stamp) >= 0; }
-
-// Wait until the prep block is complete.  Bounded like every cross-workgroup
-// wait: on a timeout the error word is raised.  With the prep kernel finished
-// before this one started (a.check == 0) there is nothing to wait for.
-__device__ __forceinline__ void wait_ready(const ChainArgs &a, int gc, int kh, int &broken) {
-    if (!a.check) return;
-    const unsigned int *f = ready_word(a, gc, kh);
-    uint32_t n = 0;
-    while (!stamp_ok(a, __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-        if (broken || ++n > kSpinLimit) {
-            if (!broken) atomicOr(a.err, 1u);
-            broken = 1;
-            return;
-        }
-        __builtin_amdgcn_s_sleep(2);
-    }
-}
-
-// SEG = false: the sequential pass over whole sequences (state_in -> outputs, state_out).
-// SEG = true: the first pass of the two-level scan.  Every segment of seg_chunks chunks
-// runs on its own, with 256 virtual value columns per head: columns 0..127 start from
-// the identity and carry no values (their state ends as the segment's transition M,
-// their read-out as R, so that O = R S_start is what the start state adds to the
-// outputs), columns 128..255 start from zero with the real values (state N, read-out
-// O0).  A segment's outputs are then O0 + R S_start and its final state M S_start + N
-// (the segment map is affine in the start state), which the two later kernels apply.
-template <int NT, bool SEG>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void chain_kernel(ChainArgs a) {
+// grid: min(items, resident slots), 512 threads
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void segment_pass_kernel(SegPassArgs a) {
+    constexpr int NT = kSegNT;
     using L = ChainLds<NT>;
     constexpr int BV = L::BV, VT = L::VT;
-    constexpr int NSL = (SEG ? 2 : 1) * kTiles / NT;
+    constexpr int NSL = 2 * kTiles / NT;        // slices of the 256 virtual columns
     constexpr int NCG = BV / 8;                 // 8-column groups per slice row
-    constexpr int NV = 8 - 2 * NT - 1;          // VALU helper waves
-    // Helper 0 runs the norm's exchange; helpers 1 and 2 gate.  With five helpers (NT = 1)
-    // conv(v) runs on helpers 3 and 4.  With three (NT = 2) the transcendental work is
-    // spread evenly instead: the conv of rows 0..31 goes to helper 0 (the conv touches LDS
-    // only, so it does not make the exchange's loads wait), rows 32..63 to helper 1, and
-    // the gating's 256 row pieces to helper 1 (64) and helper 2 (192): 48 exponentials and
-    // reciprocals per lane on helpers 1 and 2 and 32 on helper 0, against 64 on helpers 1
-    // and 2 with the conv split between them alone.
-    constexpr int kGateLanes = 128;                       // helpers 1, 2
-    constexpr int kConvBase = NT == 1 ? 192 : 0;          // first helper lane that converts v
-    constexpr int kConvLanes = 128;
-    static_assert(NV >= 3 && (NT == 2 || NV == 5), "helper roles");
-    constexpr int NRD = kC * BV * 2 / 1024;     // DMA instructions for 64 rows of raw v (or z) of the slice
-    constexpr int GROUP = kOpSlot / 1024 + 2 * NRD;  // DMA instructions the load wave issues per iteration
+    // Helpers 0..2 (waves 4, 6, 7).  The conv of rows 0..31 goes to helper 0 and of rows
+    // 32..63 to helper 1; the read-out's 256 row pieces go to helper 1 (64) and helper 2 (192).
+    constexpr int kOutLanes = 128;              // helper lanes 64..191
+    constexpr int kConvLanes = 128;             // helper lanes 0..127
+    constexpr int NRD = kC * BV * 2 / 1024;     // DMA instructions for 64 rows of raw v of the slice
+    constexpr int GROUP = kOpSlot / 1024 + NRD; // DMA instructions the load wave issues per iteration
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     _Float16 *sV = reinterpret_cast<_Float16 *>(smem + L::sV);
     float *sO = reinterpret_cast<float *>(smem + L::sO);
     uint16_t *sRawV = reinterpret_cast<uint16_t *>(smem + L::sRawV);
-    uint16_t *sZ = reinterpret_cast<uint16_t *>(smem + L::sZ);
     uint16_t *sHalo = reinterpret_cast<uint16_t *>(smem + L::sHalo);
-    float *sRstd = reinterpret_cast<float *>(smem + L::sRstd);
     float *sCW = reinterpret_cast<float *>(smem + L::sCW);
-    float *sNW = reinterpret_cast<float *>(smem + L::sNW);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches are scalar
     const int l16 = lane & 15, lq = lane >> 4;
-    // Waves w and w + 4 share a SIMD.  The state waves (0 .. NT-1) are paired with the lightest
-    // roles, the load wave and helper 0 (the norm exchange): with NT = 2 they sit at 4 and 5,
-    // with NT = 1 the load wave sits at 4 (beside the state wave) and helper 0 at 5 (beside the
-    // read-out wave); the other helpers take the remaining waves in order.
-    constexpr int kLoadWave = NT == 1 ? 4 : 5, kNormWave = NT == 1 ? 5 : 4;
+    // Waves w and w + 4 share a SIMD: the state waves (0, 1) are paired with the lightest
+    // roles, helper 0 (conv only) at 4 and the load wave at 5.
+    constexpr int kLoadWave = 5;
     const bool is_a = wave < NT, is_b = wave >= NT && wave < 2 * NT, is_l = wave == kLoadWave;
-    const int vh = wave == kNormWave ? 0
-                   : NT == 1     ? (wave < 4 ? wave - 1 : wave - 3)   // 2, 3, 6, 7 -> 1, 2, 3, 4
-                                 : wave - 5;                          // 6, 7 -> 1, 2
-    int broken = 0;
+    const int vh = wave == 4 ? 0 : wave - 5;    // helper index of waves 4, 6, 7
     __shared__ int s_item;
-    // Work items (chain, slice) come from eight queues, one per XCD: chain c
-    // sits in queue c % 8 and its slices are consecutive tickets.  A workgroup
-    // serves the queue of the XCD it runs on (the slices of a chain then share
-    // that XCD's L2), and the other queues once its own is empty.  Tickets are
-    // taken only when a workgroup starts an item, so the items begun form a
-    // prefix of every queue: the slices a workgroup waits for are either
-    // running or next in line for the next free workgroup, and no launch-wide
-    // co-residency is needed.
+    // Work items (segment chain, slice) come from eight queues, one per XCD: chain c sits
+    // in queue c % 8 and its slices are consecutive tickets.  A workgroup serves the queue
+    // of the XCD it runs on (the slices of a chain then share that XCD's L2), and the other
+    // queues once its own is empty.  No workgroup ever waits for another one.
     const int xcc = static_cast<int>(xcc_id() & 7u);
-    const int n_chains = a.B * a.Hv * (SEG ? a.nseg : 1);  // (head, segment) pairs in the segment pass
-    const bool norm = !SEG && a.norm;                       // the segment pass leaves the norm to the last kernel
+    const int n_chains = a.B * a.Hv * a.nseg;  // (head, segment) pairs
     int qi = 0;
 
     for (;;) {
@@ -842,30 +757,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         __syncthreads();
         if (item < 0) break;
         const int vchain = item / NSL, s = item % NSL;
-        const int chain = SEG ? vchain / a.nseg : vchain, seg = SEG ? vchain % a.nseg : 0;
+        const int chain = vchain / a.nseg, seg = vchain % a.nseg;
         const int b = chain / a.Hv, h = chain % a.Hv, kh = h / a.r;
-        const SeqInfo si = seq_info(a.cu, b, a.T, a.nch, a.B);  // the whole sequence
-        SeqInfo ss = si;                                    // the stretch this item runs over
-        if (SEG) {
+        const SeqInfo si = seq_info(nullptr, b, a.T, a.nch, a.B);  // the whole sequence (an even batch)
+        SeqInfo ss = si;                                             // the segment
+        {
             const int cb = seg * a.seg_chunks;
             ss.tok0 = si.tok0 + (size_t)cb * kC;
             ss.T = min(si.T - cb * kC, a.seg_chunks * kC);
             ss.c0 = si.c0 + cb;
             ss.nch = min(si.nch - cb, a.seg_chunks);
         }
-        const int nch = ss.nch, sc0 = ss.c0;
-        const int vcol0 = s * BV;                 // virtual column (0..255 in the segment pass)
-        const bool mcol = SEG && vcol0 < kD;      // transition columns: identity start, no values
+        const int nch = ss.nch, sc0 = ss.c0;      // at least one chunk: the plan leaves no segment empty
+        const int vcol0 = s * BV;                 // virtual column 0..255
+        const bool mcol = vcol0 < kD;             // transition columns: identity start, no values
         const int sv0 = vcol0 % kD;               // value column of the slice
-        const int last = nch + 2 + kLag;
+        const int last = nch + 2 + kSegLag;
         const size_t qk_stride = (size_t)a.Hk * kQKF, tp_stride = (size_t)a.Hv * kTPF;
         const _Float16 *qk0 = a.qkf + ((size_t)sc0 * a.Hk + kh) * kQKF;
         const _Float16 *tp0 = a.tpf + ((size_t)sc0 * a.Hv + h) * kTPF;
 
-        if (nch == 0) {
-            // a packed sequence with invalid bounds: flagged, nothing read or written
-            if (tid == 0) atomicOr(a.err, 2u);
-        } else if (is_a) {
+        if (is_a) {
             // ---------------------------------------------------------- state wave
             const int jc = 16 * wave + l16;
             // transposing-read lane offset (fp16 elements): row j = l16 / 4 of the 16-lane
@@ -873,22 +785,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // swizzled LDS position
             const int trofs = kswz((4 * lq + (l16 >> 2)) + 16 * (l16 & 3)) * 8;
             StateFrags fr;
-            wait_ready(a, sc0, kh, broken);
             state_load(fr, tp0, lane, lq);
             floatx4 S[8];
-            if (SEG) {
 #pragma unroll
-                for (int ti = 0; ti < 8; ++ti)
+            for (int ti = 0; ti < 8; ++ti)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) S[ti][e] = (mcol && 16 * ti + 4 * lq + e == sv0 + jc) ? 1.0f : 0.0f;
-            } else {
-                const float *src = a.state_in ? a.state_in + (size_t)chain * kD * kD : nullptr;
-#pragma unroll
-                for (int ti = 0; ti < 8; ++ti)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        S[ti][e] = src ? src[(size_t)(16 * ti + 4 * lq + e) * kD + sv0 + jc] : 0.0f;
-            }
+                for (int e = 0; e < 4; ++e) S[ti][e] = (mcol && 16 * ti + 4 * lq + e == sv0 + jc) ? 1.0f : 0.0f;
             lds_barrier();
             lds_barrier();
             for (int c = 0; c <= last; ++c) {
@@ -896,24 +798,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     state_step<NT>(smem, S, fr, tp0 + min(c + 1, nch - 1) * tp_stride, c, wave, lane, jc, lq, trofs);
                 lds_barrier();
             }
-            if (SEG) {
 #pragma unroll
-                for (int ti = 0; ti < 8; ++ti)
+            for (int ti = 0; ti < 8; ++ti)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        a.seg_state[((size_t)vchain * kD + 16 * ti + 4 * lq + e) * (2 * kD) + vcol0 + jc] = S[ti][e];
-            } else {
-#pragma unroll
-                for (int ti = 0; ti < 8; ++ti)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        a.state_out[(size_t)chain * kD * kD + (size_t)(16 * ti + 4 * lq + e) * kD + sv0 + jc] = S[ti][e];
-            }
+                for (int e = 0; e < 4; ++e)
+                    a.seg_state[((size_t)vchain * kD + 16 * ti + 4 * lq + e) * (2 * kD) + vcol0 + jc] = S[ti][e];
         } else if (is_b) {
-            // ---------------------------------------------------------- output wave
+            // ---------------------------------------------------------- read-out wave
             const int t = wave - NT, jc = 16 * t + l16;
             OutFrags fr;
-            wait_ready(a, sc0, kh, broken);
             out_load(fr, qk0, tp0, lane, lq);
             lds_barrier();
             lds_barrier();
@@ -926,13 +819,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         } else if (is_l) {
             // ---------------------------------------------------------- load wave (DMA only)
-            // raw v / z rows of chunk cc: a buffer from the chunk's first token, so rows past T read as 0;
+            // raw v rows of chunk cc: a buffer from the chunk's first token, so rows past T read as 0;
             // lane -> row (64 / NRD rows per instruction), 8-column group
-            auto rows_dma = [&](const uint16_t *x, int cc, uint16_t *dst) __attribute__((always_inline)) {
+            auto rows_dma = [&](int cc, uint16_t *dst) __attribute__((always_inline)) {
                 const int c0 = min(max(cc, 0), nch - 1) * kC;
                 const unsigned int nrow = (unsigned int)min(ss.T - c0, kC);
                 const __amdgpu_buffer_rsrc_t r =
-                    make_rsrc(x + (ss.tok0 + c0) * a.Hv * kD, nrow * (unsigned int)a.Hv * kD * 2);
+                    make_rsrc(a.v + (ss.tok0 + c0) * a.Hv * kD, nrow * (unsigned int)a.Hv * kD * 2);
 #pragma unroll
                 for (int u = 0; u < NRD; ++u) {
                     const int i = lane + 64 * u, row = i / NCG, cg = i % NCG;
@@ -946,67 +839,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int f = 0; f < 16; ++f) dma16(kb + f * kFrag + kswz(lane) * 8, slot + f * 1024);
             };
-            const uint16_t *zsrc = norm ? a.z : a.v;
-            // prologue: operands of chunks 0..D, raw v of chunks 0..D+1.  The load wave is the
-            // one that waits for the prep blocks: A and B load a chunk's operands only after the
-            // barrier that follows its wait.
-            if (a.check) {  // chunks 0..D: all stamps requested at once, one memory round trip
-                unsigned int w[L::D + 1];
+            // prologue: operands of chunks 0 and 1, raw v of chunks 0..2
+            ops_dma(0);
+            ops_dma(1);
 #pragma unroll
-                for (int j = 0; j <= L::D; ++j)
-                    w[j] = __hip_atomic_load(ready_word(a, sc0 + min(j, nch - 1), kh), __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                for (int j = 0; j <= L::D; ++j)
-                    if (j < nch && !stamp_ok(a, w[j])) wait_ready(a, sc0 + j, kh, broken);
-            }
-#pragma unroll
-            for (int j = 0; j <= L::D; ++j) ops_dma(j);
-            // a chunk's stamp is requested two iterations before it is needed, so that waiting
-            // for the previous iteration's DMA group never waits for a stamp load as well.  The
-            // load is issued in every iteration, past the last chunk from the last chunk's word
-            // (that value is never tested): the group wait below counts it, and a skipped load
-            // would let the previous group's last DMA still be in flight after the wait.
-            // (The word's offset gets a zero the compiler cannot see through: the value then counts
-            // as per-lane and stays in a vector register, which nothing waits for until the test.
-            // As a wave-uniform value it would be moved to a scalar register right after the load,
-            // and that move waits for every load in flight, the DMA groups included.)
-            int zero_v;
-            asm volatile("v_mov_b32 %0, 0" : "=v"(zero_v));
-            auto stamp_load = [&](int cc) __attribute__((always_inline)) {
-                return __hip_atomic_load(ready_word(a, sc0 + min(cc, nch - 1), kh) + zero_v, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-            };
-            // two stamp registers used in turn (iteration c reads and refills the one of its
-            // parity), so no in-flight load is ever copied between registers
-            unsigned int stamp_e = stamp_load(1 + L::D), stamp_o = stamp_load(2 + L::D);  // chunk c+1+D, even / odd c
-#pragma unroll
-            for (int j = 0; j <= L::D + 1; ++j) rows_dma(a.v, j, sRawV + j * kC * BV);
+            for (int j = 0; j <= 2; ++j) rows_dma(j, sRawV + j * kC * BV);
             wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_s_barrier();
-            auto iter = [&](int c, unsigned int &st) __attribute__((always_inline)) {
-                // (kept in program order: a stamp test moved into the previous iteration's DMA
-                // group would make the wave wait for that whole group)
-                __builtin_amdgcn_sched_barrier(0);
-                // this iteration's group: operands of chunk c+1+D, raw v of chunk c+2+D, z of
-                // chunk c-2-kLag+D
-                if (a.check && c + 1 + L::D < nch && !stamp_ok(a, st)) wait_ready(a, sc0 + c + 1 + L::D, kh, broken);
-                st = stamp_load(c + 3 + L::D);
-                ops_dma(c + 1 + L::D);
-                rows_dma(a.v, c + 2 + L::D, sRawV + modn<L::NSLOT>(c + 2 + L::D) * kC * BV);
-                rows_dma(zsrc, c - 2 - kLag + L::D, sZ + modn<L::NSLOT>(c - 2 - kLag + L::D) * kC * BV);
-                // the group of iteration c+1-D has landed (the last D groups, stamp loads
-                // included, may still be in flight)
-                wait_vmcnt<L::D * (GROUP + 1)>();
+            for (int c = 0; c <= last; ++c) {
+                // this iteration's group (the same instructions in every iteration, past the last
+                // chunk from the last chunk's rows, so that the count below is exact): operands of
+                // chunk c+2, raw v of chunk c+3
+                ops_dma(c + 2);
+                rows_dma(c + 3, sRawV + ((c + 3) % L::NSLOT) * kC * BV);
+                // the group of iteration c has landed; this one may still be in flight
+                wait_vmcnt<GROUP>();
                 __builtin_amdgcn_s_barrier();
-            };
-            int c = 0;
-            for (; c + 1 <= last; c += 2) {
-                iter(c, stamp_e);
-                iter(c + 1, stamp_o);
             }
-            if (c <= last) iter(c, stamp_e);
             wait_vmcnt<0>();
         } else {
             // ---------------------------------------------------------- VALU helpers
@@ -1016,40 +866,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                 for (int t4 = 0; t4 < 4; ++t4)
                     sCW[vtid * 4 + t4] = a.conv ? bf16_to_f32(a.conv_w[(size_t)chn * 4 + t4]) : 0.0f;
-                sNW[vtid] = norm ? bf16_to_f32(a.norm_w[sv0 + vtid]) : 1.0f;
             }
-            // conv-state rows (or zeros): the three raw rows before chunk 0
+            // the three raw rows before the segment: the conv state in (or zeros) for the
+            // first segment, the sequence's own rows for a later one
             if (vtid >= 64 && vtid < 64 + 3 * NCG) {
                 const int r3 = (vtid - 64) / NCG, cg = (vtid - 64) % NCG;
                 uint4 rw = make_uint4(0, 0, 0, 0);
-                if (SEG && seg > 0) {  // a later segment: the raw rows before it are the sequence's own
-                    if (a.conv && !mcol)
+                if (a.conv && !mcol) {
+                    if (seg > 0)
                         rw = *reinterpret_cast<const uint4 *>(a.v + ((ss.tok0 - 3 + r3) * a.Hv + h) * kD + sv0 + cg * 8);
-                } else if (a.conv && a.conv_state_in && !mcol) {
-                    rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + r3) * a.Cc + 2 * a.Hk * kD +
-                                                          h * kD + sv0 + cg * 8);
+                    else if (a.conv_state_in)
+                        rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + r3) * a.Cc +
+                                                              2 * a.Hk * kD + h * kD + sv0 + cg * 8);
                 }
                 *reinterpret_cast<uint4 *>(sHalo + r3 * BV + cg * 8) = rw;
             }
-            // A lane always serves the same 8-column group (every helper role's lane count is a
-            // multiple of 64, hence of NCG), so its conv taps and norm weights live in registers
-            // once the prologue has staged them.
-            const int cgl = vtid % NCG;
-            float nw[8];
+            const int cgl = vtid % NCG;  // a lane always serves the same 8-column group
             // conv + SiLU of v for chunk cc (its raw rows from the ring, the three rows before it
             // from sHalo[cc & 1]) -> sV[cc & 1]; the chunk's last three raw rows -> sHalo[(cc + 1) & 1].
-            // Conv lane ci owns RPI consecutive rows of 4 channels: it reads each raw row it needs
-            // once (RPI + 3 rows of 8 bytes) and writes each channel's RPI outputs as one packed
-            // store, RPI = 2 with one tile and 4 with two, so that every conv lane has one item.
-            constexpr int RPI = NT == 1 ? 2 : 4;
+            // Conv lane ci owns RPI = 4 consecutive rows of 4 channels: it reads each raw row it
+            // needs once (RPI + 3 rows of 8 bytes) and writes each channel's RPI outputs as one
+            // packed store.
+            constexpr int RPI = 4;
             constexpr int NC4 = BV / 4;
             static_assert((kC / RPI) * NC4 == kConvLanes, "one conv item per conv lane");
-            const int ci = vtid >= kConvBase && vtid < kConvBase + kConvLanes ? vtid - kConvBase : -1;  // conv lane
+            const int ci = vtid < kConvLanes ? vtid : -1;  // conv lane
             const int c4 = (ci > 0 ? ci : 0) % NC4, rg = (ci > 0 ? ci : 0) / NC4;
             float hwc[16];  // conv taps of the lane's 4 channels: tap j of channel e at 4 e + j
             auto conv_v = [&](int cc) __attribute__((always_inline)) {
                 if (ci < 0) return;  // not a converting helper
-                const uint16_t *raw = sRawV + modn<L::NSLOT>(cc) * kC * BV;
+                const uint16_t *raw = sRawV + (cc % L::NSLOT) * kC * BV;
                 if (ci < 3 * NCG) {
                     const int r3 = ci / NCG, cg = ci % NCG;
                     *reinterpret_cast<uint4 *>(sHalo + ((cc + 1) & 1) * 3 * BV + r3 * BV + cg * 8) =
@@ -1097,134 +943,52 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
                 _Float16 *dst = sV + (cc & 1) * BV * P64 + c4 * 4 * P64 + r0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (RPI == 2) {
-                        *reinterpret_cast<halfx2 *>(dst + e * P64) =
-                            halfx2{static_cast<_Float16>(u[0][e]), static_cast<_Float16>(u[1][e])};
-                    } else {
-                        *reinterpret_cast<half4 *>(dst + e * P64) =
-                            half4{static_cast<_Float16>(u[0][e]), static_cast<_Float16>(u[1][e]),
-                                  static_cast<_Float16>(u[2][e]), static_cast<_Float16>(u[3][e])};
-                    }
-                }
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<half4 *>(dst + e * P64) =
+                        half4{static_cast<_Float16>(u[0][e]), static_cast<_Float16>(u[1][e]),
+                              static_cast<_Float16>(u[2][e]), static_cast<_Float16>(u[3][e])};
             };
-            // gated RMSNorm + store of chunk oc
-            auto gate = [&](int oc) __attribute__((always_inline)) {
+            // the raw read-out of chunk oc to the workspace for the last kernel (every row: rows
+            // past T are finite): R as two 4-column pieces of one row in two lanes of a fragment,
+            // O0 as 8 columns of one row
+            auto emit = [&](int oc) __attribute__((always_inline)) {
                 const float *src = sO + (oc % kORing) * VT + cgl * 8 * PL;
-                const float *rs = sRstd + (oc & 1) * kC;
-                const uint16_t *zt = sZ + modn<L::NSLOT>(oc) * kC * BV + cgl * 8;
-                // NT = 1: one row piece per gating lane; NT = 2: helper 1 one, helper 2 three
-                const int gstep = NT == 1 ? kGateLanes : (vh == 1 ? kC * NCG : 64);
+                _Float16 *blk = a.seg_out + ((size_t)(sc0 + oc) * a.Hv + h) * kSegBlk;
+                const int col = sv0 + cgl * 8;
+                const int gstep = vh == 1 ? kC * NCG : 64;  // helper 1 one row piece per lane, helper 2 three
 #pragma unroll 1
                 for (int it = vtid - 64; it < kC * NCG; it += gstep) {
                     const int row = it / NCG;
-                    const int tt = oc * kC + row;
                     float y[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) y[e] = src[e * PL + row];
-                    const uint4 zr = *reinterpret_cast<const uint4 *>(zt + row * BV);
-                    const float rstd = rs[row];
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (SEG) {  // the raw read-out, for the last kernel (every row: rows past T are finite)
-                        _Float16 *blk = a.seg_out + ((size_t)(sc0 + oc) * a.Hv + h) * kSegBlk;
-                        const int col = sv0 + cgl * 8;
-                        if (mcol) {  // R: two 4-column pieces of one row, in two lanes of a fragment
-                            const int cc = col & 31, L0 = (row & 15) + 16 * ((cc & 15) >> 2);
-                            _Float16 *f = blk + (((row >> 4) * 4 + (col >> 5)) * 64 + L0) * 8 + 4 * (cc >> 4);
-                            *reinterpret_cast<half4 *>(f) = half4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2],
-                                                                  (_Float16)y[3]};
-                            *reinterpret_cast<half4 *>(f + 16 * 8) = half4{(_Float16)y[4], (_Float16)y[5],
-                                                                           (_Float16)y[6], (_Float16)y[7]};
-                        } else {     // O0: 8 columns of one row
-                            *reinterpret_cast<half8 *>(blk + kSegR + row * kD + col) =
-                                half8{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3],
-                                      (_Float16)y[4], (_Float16)y[5], (_Float16)y[6], (_Float16)y[7]};
-                        }
-                        continue;
+                    if (mcol) {
+                        const int cc = col & 31, L0 = (row & 15) + 16 * ((cc & 15) >> 2);
+                        _Float16 *f = blk + (((row >> 4) * 4 + (col >> 5)) * 64 + L0) * 8 + 4 * (cc >> 4);
+                        *reinterpret_cast<half4 *>(f) = half4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2],
+                                                              (_Float16)y[3]};
+                        *reinterpret_cast<half4 *>(f + 16 * 8) = half4{(_Float16)y[4], (_Float16)y[5],
+                                                                       (_Float16)y[6], (_Float16)y[7]};
+                    } else {
+                        *reinterpret_cast<half8 *>(blk + kSegR + row * kD + col) =
+                            half8{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3],
+                                  (_Float16)y[4], (_Float16)y[5], (_Float16)y[6], (_Float16)y[7]};
                     }
-                    if (norm) {
-                        float zf[8], t8[8];
-                        unpack_bf16x8(zr, zf);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) t8[e] = __builtin_amdgcn_exp2f(zf[e] * -1.4426950408889634f);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) t8[e] = __builtin_amdgcn_rcpf(1.0f + t8[e]);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) y[e] = nw[e] * (y[e] * rstd) * (zf[e] * t8[e]);
-                    }
-                    if (tt < ss.T)
-                        *reinterpret_cast<uint4 *>(a.o + ((ss.tok0 + tt) * a.Hv + h) * kD + sv0 + cgl * 8) =
-                            pack_bf16x8(y);
                 }
             };
-            unsigned long long *mrow = a.mbox + (size_t)chain * kTiles * kRing * kC + lane;  // row = lane
             lds_barrier();
 #pragma unroll
             for (int e = 0; e < 16; ++e) hwc[e] = sCW[c4 * 16 + e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) nw[e] = sNW[cgl * 8 + e];
             conv_v(0);
             lds_barrier();
-            // Helper 0 owns the norm's cross-slice exchange and issues no output stores;
-            // the others gate and store.  On this target one counter tracks both loads and
-            // stores, so a wave that waits for a load also waits for every store it issued
-            // before it: keeping the mailbox loads and the output stores in different waves
-            // keeps either from waiting on the other.
-            if (vh == 0) {
-                unsigned long long mbn[NSL] = {};  // sibling words of chunk rc, requested an iteration early
-                auto mb_request = [&](int cc) __attribute__((always_inline)) {
-                    if (norm && cc >= 0 && cc < nch) {
-#pragma unroll
-                        for (int sib = 0; sib < NSL; ++sib)
-                            mbn[sib] = __hip_atomic_load(mrow + ((size_t)sib * kRing + (cc % kRing)) * kC,
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                };
-                mb_request(-2 - kLag);
-                for (int c = 0; c <= last; ++c) {
-                    if (NT == 2 && c + 1 < nch) conv_v(c + 1);  // rows 0..31 of the conv
-                    // 1/rms of chunk rc from the siblings' words (published kLag - 1 iterations before
-                    // they were requested; a word without the chunk's tag is waited for)
-                    const int rc = c - 2 - kLag;
-                    if (norm && rc >= 0 && rc < nch) {
-                        float tot = 0.0f;
-#pragma unroll
-                        for (int sib = 0; sib < NSL; ++sib) {
-                            if ((uint32_t)(mbn[sib] >> 32) != (uint32_t)(rc + 1))
-                                mbn[sib] = spin_load(mrow + ((size_t)sib * kRing + (rc % kRing)) * kC,
-                                                     (uint32_t)(rc + 1), a.err, broken);
-                            tot += __uint_as_float((uint32_t)mbn[sib]);
-                        }
-                        sRstd[(rc & 1) * kC + lane] = __builtin_amdgcn_rsqf(tot * (1.0f / kD) + a.eps_norm);
-                    }
-                    // row sums of chunk c-2 over this slice's columns -> mailbox (tag c-1)
-                    if (norm && c >= 2 && c - 2 < nch) {
-                        const float *src = sO + ((c - 2) % kORing) * VT + lane;
-                        float ov[BV];
-#pragma unroll
-                        for (int j = 0; j < BV; ++j) ov[j] = src[j * PL];
-                        __builtin_amdgcn_sched_barrier(0);
-                        float ss = 0.0f;
-#pragma unroll
-                        for (int j = 0; j < BV; ++j) ss += ov[j] * ov[j];
-                        unsigned long long *mb =
-                            a.mbox + (((size_t)chain * kTiles + s) * kRing + ((c - 2) % kRing)) * kC + lane;
-                        __hip_atomic_store(mb, ((unsigned long long)(uint32_t)(c - 1) << 32) | __float_as_uint(ss),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                    mb_request(rc + 1);
-                    lds_barrier();
-                }
-            } else {
-                for (int c = 0; c <= last; ++c) {
-                    if (c + 1 < nch) conv_v(c + 1);  // nothing for a lane without a conv item
-                    const int oc = c - 3 - kLag;
-                    if (vtid < 64 + kGateLanes && oc >= 0 && oc < nch) gate(oc);
-                    lds_barrier();
-                }
+            for (int c = 0; c <= last; ++c) {
+                if (c + 1 < nch) conv_v(c + 1);  // nothing for a lane without a conv item
+                const int oc = c - 3 - kSegLag;
+                if (vtid >= 64 && vtid < 64 + kOutLanes && oc >= 0 && oc < nch) emit(oc);
+                lds_barrier();
             }
-            // raw v inputs of the last three tokens -> conv state out
-            if (vh == 0 && a.conv && a.conv_state_out && lane < 3 * NCG && !mcol && (!SEG || seg == a.nseg - 1)) {
+            // raw v inputs of the sequence's last three tokens -> conv state out
+            if (vh == 0 && a.conv && a.conv_state_out && lane < 3 * NCG && !mcol && seg == a.nseg - 1) {
                 const int sidx = lane / NCG, cg = lane % NCG;
                 const int tau = si.T - 3 + sidx;
                 const int ch = 2 * a.Hk * kD + h * kD + sv0 + cg * 8;
@@ -1234,26 +998,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 else if (a.conv_state_in)
                     rw = *reinterpret_cast<const uint4 *>(a.conv_state_in + ((size_t)b * 3 + (3 + tau)) * a.Cc + ch);
                 *reinterpret_cast<uint4 *>(a.conv_state_out + ((size_t)b * 3 + sidx) * a.Cc + ch) = rw;
-            }
-        }
-
-        // ---- the last slice of a chain to finish clears the chain's mailbox.  Relaxed order
-        // suffices and avoids an L2 write-back per item: every mailbox word is accessed only by
-        // agent-scope atomics, and a slice's last mailbox read has returned (its value was used
-        // before the loop's final barrier) before its count goes up.
-        if (norm) {
-            __shared__ unsigned int last_one;
-            if (tid == 0) {
-                const unsigned int old =
-                    __hip_atomic_fetch_add(a.counters + chain, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                last_one = (old == NSL - 1) ? 1u : 0u;
-            }
-            lds_barrier();
-            if (last_one) {
-                unsigned long long *mb = a.mbox + (size_t)chain * kTiles * kRing * kC;
-                for (int i = tid; i < kTiles * kRing * kC; i += 512)
-                    __hip_atomic_store(mb + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (tid == 0) __hip_atomic_store(a.counters + chain, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         lds_barrier();
@@ -1433,10 +1177,11 @@ int device_facts(DeviceFacts **out) {
     return 0;
 }
 
-// Launch shape of the two-level scan's first pass (chain_kernel<2, true>).
-int seg_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
-    constexpr size_t lds = ChainLds<2>::bytes;
-    auto fn = chain_kernel<2, true>;
+// Launch shape of the two-level scan's first pass: as many workgroups as items, at most
+// one round of resident ones (no workgroup waits for another, so any number runs correctly).
+int seg_launch_shape(const SegPassArgs &a, ChainLaunch *cl) {
+    constexpr size_t lds = ChainLds<kSegNT>::bytes;
+    const void *fn = reinterpret_cast<const void *>(segment_pass_kernel);
     DeviceFacts *df;
     int rc = device_facts(&df);
     if (rc) return rc;
@@ -1451,20 +1196,17 @@ int seg_launch_shape(const ChainArgs &a, ChainLaunch *cl) {
                 return fail("hipDeviceGetAttribute(multiprocessor count)", e);
         }
         if (!df->seg_per_cu) {
-            if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         (int)lds)) != hipSuccess)
-                return fail("hipFuncSetAttribute(chain_kernel)", e);
-            if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&df->seg_per_cu, reinterpret_cast<const void *>(fn), 512,
-                                                                  lds)) != hipSuccess)
-                return fail("hipOccupancyMaxActiveBlocksPerMultiprocessor(chain_kernel)", e);
+            if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+                return fail("hipFuncSetAttribute(segment_pass_kernel)", e);
+            if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&df->seg_per_cu, fn, 512, lds)) != hipSuccess)
+                return fail("hipOccupancyMaxActiveBlocksPerMultiprocessor(segment_pass_kernel)", e);
         }
         ncu = df->ncu;
         per_cu = df->seg_per_cu;
     }
-    constexpr int NSL = 2 * kTiles / 2;
     const int cap = ncu * per_cu;
-    if (cap < 8 * NSL) return fail("chain_kernel: fewer resident workgroup slots than eight heads' slices");
-    cl->fn = reinterpret_cast<const void *>(fn);
+    if (cap < 1) return fail("segment_pass_kernel: no resident workgroup fits a compute unit");
+    cl->fn = fn;
     cl->lds = lds;
     cl->grid = a.n_items < cap ? a.n_items : cap;
     cl->ncu = ncu;
@@ -1485,8 +1227,8 @@ int plan_prefill(int B, int T, int Hk, int Hv, bool packed, int segments, Prefil
     plan->nslots = packed ? (long long)(T / kC) + B : (long long)B * plan->nchunks;
     // one row of mailbox words per (sequence, value head, slice, ring slot), and one more set
     // past them that the sequential pass publishes into outside a sequence's chunk range
-    plan->mbox_bytes = align256((size_t)(chains + 1) * kTiles * kRing * kC * sizeof(unsigned long long));
-    plan->xch_bytes = kHeaderBytes + plan->mbox_bytes + align256((size_t)chains * sizeof(unsigned int));
+    plan->mbox_bytes = align256((size_t)(chains + 1) * kTiles * kMboxRing * kC * sizeof(unsigned long long));
+    plan->xch_bytes = kHeaderBytes + plan->mbox_bytes;
     plan->qk_bytes = align256((size_t)plan->nslots * Hk * kQKF * sizeof(_Float16));
     plan->tp_bytes = align256((size_t)plan->nslots * Hv * kTPF * sizeof(_Float16));
     // Two-level scan (even batches): worth it when the sequential pass would leave most of
@@ -1531,7 +1273,6 @@ PrefillRegions prefill_regions(void *workspace, const PrefillPlan &plan, int B, 
     r.tickets = reinterpret_cast<unsigned int *>(ws + kTicketOffset);
     r.exits = reinterpret_cast<unsigned int *>(ws + kExitOffset);
     r.mbox = reinterpret_cast<unsigned long long *>(ws + kHeaderBytes);
-    r.counters = reinterpret_cast<unsigned int *>(ws + kHeaderBytes + plan.mbox_bytes);
     r.qkf = reinterpret_cast<_Float16 *>(ws + plan.xch_bytes);
     r.tpf = reinterpret_cast<_Float16 *>(ws + plan.xch_bytes + plan.qk_bytes);
     r.seg = ws + plan.xch_bytes + plan.qk_bytes + plan.tp_bytes;
@@ -1579,19 +1320,12 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     if (plan.nseg <= 1) return launch_pass(p, plan, rg, stream);
 
     // ---- two-level scan
-    ChainArgs a;
+    SegPassArgs a;
     a.qkf = rg.qkf; a.tpf = rg.tpf;
-    a.v = p.v; a.z = p.z; a.conv_w = p.conv_w; a.norm_w = p.norm_w; a.conv_state_in = p.conv_state_in;
-    a.state_in = p.state_in; a.o = p.o; a.conv_state_out = p.conv_state_out; a.state_out = p.state_out;
-    a.mbox = rg.mbox; a.counters = rg.counters; a.err = rg.err;
+    a.v = p.v; a.conv_w = p.conv_w; a.conv_state_in = p.conv_state_in; a.conv_state_out = p.conv_state_out;
     a.tickets = rg.tickets; a.exits = rg.exits;
-    // the prep kernel has finished before this launch starts: the load wave's readiness loads
-    // read valid memory (the operand blocks) and their values are never tested (check = 0)
-    a.ready = reinterpret_cast<const unsigned int *>(rg.qkf); a.stamp = 0; a.check = 0;
-    a.cu = p.cu_seqlens;
-    a.B = p.B; a.T = p.T; a.Hk = p.Hk; a.Hv = p.Hv; a.r = pa.r; a.Cc = pa.Cc; a.conv = pa.conv; a.norm = p.norm;
+    a.B = p.B; a.T = p.T; a.Hk = p.Hk; a.Hv = p.Hv; a.r = pa.r; a.Cc = pa.Cc; a.conv = pa.conv;
     a.nch = plan.nchunks; a.grid = 0;
-    a.eps_norm = p.eps_norm;
     a.seg_out = reinterpret_cast<_Float16 *>(rg.seg);
     a.seg_state = reinterpret_cast<float *>(rg.seg + plan.seg_out_bytes);
     a.nseg = plan.nseg; a.seg_chunks = plan.seg_chunks;
@@ -1601,7 +1335,7 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     a.grid = cl.grid;
     void *cargs[] = {&a};
     if ((e = hipLaunchKernel(cl.fn, dim3(cl.grid), dim3(512), cargs, cl.lds, stream)) != hipSuccess)
-        return fail("hipLaunchKernel(chain_kernel)", e);
+        return fail("hipLaunchKernel(segment_pass_kernel)", e);
     SegArgs sa;
     sa.state_in = p.state_in; sa.seg_state = a.seg_state;
     sa.seg_frag = reinterpret_cast<_Float16 *>(rg.seg + plan.seg_out_bytes + plan.seg_state_bytes);

@@ -9,6 +9,7 @@ namespace {
 constexpr int kD = 128;        // head width
 constexpr int kC = 64;         // chunk length
 constexpr int kTiles = 8;      // 16-column tiles per head
+constexpr int kMboxRing = 8;   // gated-norm mailbox slots per (head, 16-column tile)
 constexpr uint32_t kSpinLimit = 1u << 20;  // bound of every cross-workgroup wait (~0.3 s)
 
 // LDS pitches (elements) so that 16-row MFMA fragment reads hit distinct banks.
@@ -85,24 +86,14 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// Stores of operands that the sequential pass may read while the prep kernel
-// still runs: written through to memory (agent-coherent, the encoding of an
-// agent-scope relaxed atomic store), so a block can publish its stamp after its
-// stores complete without writing back a whole L2.
-// Workspace stores of the prep kernel: written through to memory (sc1) when the sequential
-// pass may read them while the prep kernel still runs, ordinary stores otherwise (the
-// kernel boundary then orders them).
-constexpr int kWriteThrough = 16;  // sc1
+// A 16-byte or 4-byte store into the workspace through a buffer resource.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-template <bool THROUGH>
 __device__ __forceinline__ void st_ws(__amdgpu_buffer_rsrc_t r, int voff, half8 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, THROUGH ? kWriteThrough : 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, 0);
 }
-template <bool THROUGH>
 __device__ __forceinline__ void st_ws(__amdgpu_buffer_rsrc_t r, int voff, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, THROUGH ? kWriteThrough : 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, 0, 0);
 }
-
 // 4 fp16 from LDS through the transposing read: within each 16-lane group the
 // lanes' 8-byte chunks form a 4 x 16 matrix (row = lane / 4, column = 4 (lane % 4)
 // + element) and lane i receives column i.
