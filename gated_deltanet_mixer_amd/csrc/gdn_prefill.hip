@@ -93,9 +93,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave bases stay scalar
     const int l16 = lane & 15, lq = lane >> 4;
-    // blocks in chunk-major order (chunk gc of all sequences, numbered sequence by
-    // sequence), so the sequential pass can start on the first chunks while later ones are
-    // still being prepared
+    // blocks in chunk-major order: operand slot gc (chunk of a sequence, numbered sequence by
+    // sequence), key head kh
     const int gc = blockIdx.x / a.Hk, kh = blockIdx.x % a.Hk;
     // the exchange area (error word, queue tickets, mailbox) starts every call at zero
     for (size_t i = (size_t)blockIdx.x * 256 + tid; i < a.clear_n16; i += (size_t)gridDim.x * 256)
