@@ -54,6 +54,12 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&f)[8]) {
 
 // ---------------------------------------------------------------- math
 
+// a.lo * b.lo + a.hi * b.hi + c for two bf16 pairs, accumulated in fp32 (v_dot2c_f32_bf16)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ float bf16_dot2(unsigned int a, unsigned int b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // x * sigmoid(x) in fp32 from the hardware base-2 exponential and reciprocal
 // (v_exp_f32, v_rcp_f32: about 1 ulp each).  Saturates correctly: a large
 // negative x gives exp2 -> inf, rcp -> 0.
@@ -87,6 +93,23 @@ __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
     for (int o = W / 2; o >= 1; o >>= 1)
         v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// v of another lane of the same 16-lane row, through the DPP operand modifier (no LDS)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each row of 16 lanes (lanes 16 k .. 16 k + 15), every lane of the row receiving
+// the same bits: each step adds two equal partial sums, in either order, across a quad, a
+// half-row and the row (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
     return v;
 }
 

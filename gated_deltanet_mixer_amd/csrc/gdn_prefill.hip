@@ -162,49 +162,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                                     : make_uint4(0, 0, 0, 0);
             }
         }
+        // conv taps as bf16 pairs: word 2 e holds taps 0, 1 of channel e, word 2 e + 1 taps 2, 3
         uint4 wr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             wr[i] = a.conv ? reinterpret_cast<const uint4 *>(a.conv_w + (size_t)ch * 4)[i] : make_uint4(0, 0, 0, 0);
-        float w[32];  // w[4 e + j]: tap j (row t - 3 + j) of channel e
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float tmp[8];
-            unpack_bf16x8(wr[i], tmp);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w[8 * i + e] = tmp[e];
-        }
+        const unsigned int wp[16] = {wr[0].x, wr[0].y, wr[0].z, wr[0].w, wr[1].x, wr[1].y, wr[1].z, wr[1].w,
+                                     wr[2].x, wr[2].y, wr[2].z, wr[2].w, wr[3].x, wr[3].y, wr[3].z, wr[3].w};
         const float qscale = m ? 1.0f : 0.08838834764831845f;  // 1/sqrt(128) on q
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tl0 = (seg0 + 8 * u) * 4;  // local token of the segment
-            float x[7][8];
-#pragma unroll
-            for (int rr = 0; rr < 7; ++rr) unpack_bf16x8(xr[u][rr], x[rr]);
             float uu[4][8];
             if (a.conv) {
+                // The conv as bf16 dot products of tap pairs (the products are exact in fp32):
+                // xp[rr][e] pairs channel e of rows rr and rr + 1, so output row i of channel e is
+                // dot(taps 0-1, xp[i][e]) + dot(taps 2-3, xp[i + 2][e]).
+                unsigned int xw[7][4];
+#pragma unroll
+                for (int rr = 0; rr < 7; ++rr) {
+                    xw[rr][0] = xr[u][rr].x; xw[rr][1] = xr[u][rr].y; xw[rr][2] = xr[u][rr].z; xw[rr][3] = xr[u][rr].w;
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        uu[i][e] = w[4 * e] * x[i][e] + w[4 * e + 1] * x[i + 1][e] + w[4 * e + 2] * x[i + 2][e] +
-                                   w[4 * e + 3] * x[i + 3][e];
+                    for (int k = 0; k < 4; ++k) {
+                        // channels 2 k (low halves) and 2 k + 1 (high halves)
+                        const unsigned int lo01 = __builtin_amdgcn_perm(xw[i + 1][k], xw[i][k], 0x05040100u);
+                        const unsigned int lo23 = __builtin_amdgcn_perm(xw[i + 3][k], xw[i + 2][k], 0x05040100u);
+                        const unsigned int hi01 = __builtin_amdgcn_perm(xw[i + 1][k], xw[i][k], 0x07060302u);
+                        const unsigned int hi23 = __builtin_amdgcn_perm(xw[i + 3][k], xw[i + 2][k], 0x07060302u);
+                        uu[i][2 * k] = bf16_dot2(wp[4 * k + 1], lo23, bf16_dot2(wp[4 * k], lo01, 0.0f));
+                        uu[i][2 * k + 1] = bf16_dot2(wp[4 * k + 3], hi23, bf16_dot2(wp[4 * k + 2], hi01, 0.0f));
+                    }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) uu[i][e] = silu(uu[i][e]);
             } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) uu[i][e] = x[i + 3][e];
+                for (int i = 0; i < 4; ++i) unpack_bf16x8(xr[u][i + 3], uu[i]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float ss = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += uu[i][e] * uu[i][e];
-                ss = group_sum<16>(ss);
+                ss = row16_sum(ss);
                 const bool valid = tc0 + tl0 + i < si.T;
                 // rows past T are zero; the hardware reciprocal square root (about 1 ulp) is far
                 // inside the fp16 the result is stored in
@@ -252,28 +256,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
     // ---- 1b. q^, k^ and k^T to the workspace as operand fragments
     {
+        // Wave w writes fragments w + 4 it: q^ for it < 4, k^ for it >= 4, each at row tile it & 3
+        // and key step w, so every source address is the lane's base plus a constant.
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.qkf + ((size_t)gc * a.Hk + kh) * kQKF, kQKF * 2);
-        for (int idx = tid; idx < 32 * 64; idx += 256) {
-            const int f = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
-            const _Float16 *M = f < 16 ? sQ : sK;
-            const int ff = f & 15;
-            const _Float16 *src = M + (16 * (ff >> 2) + fl) * P128 + 32 * (ff & 3) + 4 * fq;
-            const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
-            st_ws(rq, idx * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        const int fl = lane & 15, fq = lane >> 4;
+        {
+            const int lb = fl * P128 + 32 * wave + 4 * fq;
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const _Float16 *src = (it < 4 ? sQ : sK) + lb + 16 * (it & 3) * P128;
+                const half4 lo = lds_half4(src), hi = lds_half4(src + 16);
+                st_ws(rq, (tid + 256 * it) * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            }
         }
         // k^T fragment 32 + 2 ti + s2, lane fl + 16 fq: key 16 ti + fl at tokens
-        // 32 s2 + 4 fq + e and 32 s2 + 16 + 4 fq + e (e = 0..3)
-        for (int idx = tid; idx < 16 * 64; idx += 256) {
-            const int ft = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
-            const int ti = ft >> 1, s2 = ft & 1;
-            const _Float16 *src = sK + (32 * s2 + 4 * fq) * P128 + 16 * ti + fl;
-            half8 v;
+        // 32 s2 + 4 fq + e and 32 s2 + 16 + 4 fq + e (e = 0..3).  Wave w writes fragments
+        // 32 + w + 4 it: s2 = w & 1, ti = (w >> 1) + 2 it.
+        {
+            const _Float16 *lb = sK + (32 * (wave & 1) + 4 * fq) * P128 + 16 * (wave >> 1) + fl;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[e] = src[e * P128];
-                v[4 + e] = src[(16 + e) * P128];
+            for (int it = 0; it < 4; ++it) {
+                const _Float16 *src = lb + 32 * it;
+                half8 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = src[e * P128];
+                    v[4 + e] = src[(16 + e) * P128];
+                }
+                st_ws(rq, (32 * 64 + tid + 256 * it) * 16, v);
             }
-            st_ws(rq, (32 * 64 + idx) * 16, v);
         }
     }
 
@@ -357,7 +368,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 const float gjs[4] = {gj.x, gj.y, gj.z, gj.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    v[4 * hh + e] = static_cast<_Float16>(j0 + e <= i ? rawP[pf][hh][e] * hw_exp(gi - gjs[e]) : 0.0f);
+                    v[4 * hh + e] = static_cast<_Float16>(keep_if_nonneg(i - (j0 + e), rawP[pf][hh][e] * hw_exp(gi - gjs[e])));
             }
             st_ws(rtp, (kPOff + f * kFrag) * 2 + lane * 16, v);
         }
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const float grs[4] = {gr.x, gr.y, gr.z, gr.w}, brs[4] = {br.x, br.y, br.z, br.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                sL[(r0 + e) * PL + col] = col < r0 + e ? brs[e] * rawL[u][e] * hw_exp(grs[e] - gcol) : 0.0f;
+                sL[(r0 + e) * PL + col] = keep_if_nonneg(r0 + e - 1 - col, brs[e] * rawL[u][e] * hw_exp(grs[e] - gcol));
         }
         lds_barrier();
 
@@ -446,21 +457,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
         // T diag(beta) to the workspace as fragments 0..5: row tiles 0 and 1 take the first token
         // step only, row tiles 2 and 3 both
-        for (int idx = tid; idx < 6 * 64; idx += 256) {
-            const int f = idx >> 6, fl = idx & 15, fq = (idx >> 4) & 3;
-            const int row = f < 2 ? 16 * f + fl : 32 + 16 * ((f - 2) >> 1) + fl;
+        // (wave w writes fragments w and w + 4; the row block bi and token step ks are uniform)
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int f = wave + 4 * it;
+            if (f >= 6) break;
+            const int fl = lane & 15, fq = lane >> 4;
+            const int bi = f < 2 ? f : 2 + ((f - 2) >> 1);
             const int ks = f < 2 ? 0 : (f - 2) & 1;
-            const int bi = row >> 4;
             half8 v;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int bj = 2 * ks + hh;  // the 16-column block of these 4 columns
                 half4 q4 = {0, 0, 0, 0};
-                if (bj <= bi) q4 = lds_half4(sTbst + (bi * (bi + 1) / 2 + bj) * kBlk + (row & 15) * 16 + 4 * fq);
+                if (bj <= bi) q4 = lds_half4(sTbst + (bi * (bi + 1) / 2 + bj) * kBlk + fl * 16 + 4 * fq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }
-            st_ws(rtp, idx * 16, v);
+            st_ws(rtp, (f * 64 + lane) * 16, v);
         }
         // (no barrier: the next head writes T staging only after its own first barrier, which
         // every wave reaches after finishing these reads)
@@ -1127,7 +1141,7 @@ __global__ __launch_bounds__(256) void seg_output_kernel(SegArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int row = 16 * w + 4 * lq + e;
-        const float rstd = __builtin_amdgcn_rsqf(group_sum<16>(ss[e]) * (1.0f / kD) + a.eps_norm);
+        const float rstd = __builtin_amdgcn_rsqf(row16_sum(ss[e]) * (1.0f / kD) + a.eps_norm);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
             const int col = 16 * ct + l16;

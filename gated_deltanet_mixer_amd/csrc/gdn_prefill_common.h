@@ -162,6 +162,12 @@ __device__ __forceinline__ int find_seq(const int *cu, int B, int gc, int lane) 
 // Its arguments are log-decay sums (never positive past rounding); results that would be
 // denormal flush to zero, which the decays they stand for are to fp16 precision anyway.
 __device__ __forceinline__ float hw_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+// v when d >= 0, else +0, on the bit pattern: a select with an exponential in one arm is
+// turned into a branch around it, and per element that costs more than the exponential.
+// Where d < 0 the discarded v may be inf or NaN (an exponential of a positive argument).
+__device__ __forceinline__ float keep_if_nonneg(int d, float v) {
+    return __uint_as_float(__float_as_uint(v) & ~(unsigned int)(d >> 31));
+}
 
 __device__ __forceinline__ unsigned long long spin_load(unsigned long long *p, uint32_t tag, unsigned int *err,
                                                         int &broken) {
