@@ -305,43 +305,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         st_ws(rtp, kVecOff * 2 + 4 * (kC + lane), hw_exp(gC - gv));
         if (lane < 4) st_ws(rtp, kVecOff * 2 + 4 * (2 * kC + lane), hw_exp(gC));
     }
-    // L tiles: task tt = wave + 4 u (u = 0..2, tt < 10), lower 16x16 blocks (ti, tj) of K K^T with
-    // the accumulator lane holding column j = 16 tj + l16, rows 16 ti + 4 lq + e.
     // P fragments: operand fragment f of P (row block fI, token step fks) is built from the
     // K Q^T tiles (fI, 2 fks) and (fI, 2 fks + 1): with K as the A operand and Q as the B operand
     // the accumulator lane holds query row i = 16 fI + l16 at keys j = 16 J + 4 lq + e, which is
     // the fragment's own lane layout, so P needs no staging.  Tiles above the diagonal are zero.
-    // Wave w owns fragments kPF[w] (6 fragments, 10 nonzero tiles over the four waves).
+    // Wave w owns fragments kPF[w] (6 fragments, 10 nonzero tiles over the four waves).  The
+    // K K^T tile of L for the same (i, j) block comes from the same A operand with K as the B
+    // operand (K K^T is symmetric), so the lane holding P_ij also holds the raw L_ij and one
+    // exponential e^{G_i - G_j} serves both.
     constexpr int kPF[4][2] = {{1, 0}, {3, 2}, {4, -1}, {5, -1}};
     constexpr int kFI[6] = {0, 1, 2, 2, 3, 3}, kFKS[6] = {0, 0, 0, 1, 0, 1};
-    auto tile = [&](const _Float16 *Aop, int ai, const _Float16 *Bop, int bj) __attribute__((always_inline)) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const half8 av = lds_half8(Aop + (16 * ai + l16) * P128 + 32 * ks + 8 * lq);
-            const half8 bv = lds_half8(Bop + (16 * bj + l16) * P128 + 32 * ks + 8 * lq);
-            acc = mfma16x16x32(av, bv, acc);
-        }
-        return acc;
-    };
-    floatx4 rawL[3], rawP[2][2];
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-        const int tt = wave + 4 * u;
-        rawL[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (tt < 10) {
-            int ti, tj;
-            tri_block(tt, ti, tj);
-            rawL[u] = tile(sK, ti, sK, tj);
-        }
-    }
+    floatx4 rawP[2][2], rawL[2][2];
 #pragma unroll
     for (int pf = 0; pf < 2; ++pf) {
         const int f = kPF[wave][pf];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            rawP[pf][hh] = floatx4{0.f, 0.f, 0.f, 0.f};
-            if (f >= 0 && 2 * kFKS[f] + hh <= kFI[f]) rawP[pf][hh] = tile(sK, 2 * kFKS[f] + hh, sQ, kFI[f]);
+            rawP[pf][hh] = rawL[pf][hh] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const int J = f >= 0 ? 2 * kFKS[f] + hh : 0, fI = f >= 0 ? kFI[f] : 0;
+            if (f >= 0 && J <= fI) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const half8 av = lds_half8(sK + (16 * J + l16) * P128 + 32 * ks + 8 * lq);
+                    const half8 bq = lds_half8(sQ + (16 * fI + l16) * P128 + 32 * ks + 8 * lq);
+                    const half8 bk = lds_half8(sK + (16 * fI + l16) * P128 + 32 * ks + 8 * lq);
+                    rawP[pf][hh] = mfma16x16x32(av, bq, rawP[pf][hh]);
+                    rawL[pf][hh] = mfma16x16x32(av, bk, rawL[pf][hh]);
+                }
+            }
         }
     }
     lds_barrier();
@@ -353,40 +344,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         const float *sG = sGr + hr * kC;          // cumulative log-decay G
         const float *sB = sGr + (a.r + hr) * kC;  // beta
 
-        // P = (Q K^T) o R (lower incl. the diagonal), straight from registers to the workspace
+        // P = (Q K^T) o R (lower incl. the diagonal), straight from registers to the workspace, and
+        // L = strictly-lower(beta_i (K K^T) o R) (fp32) to LDS rows, from the same exponentials
 #pragma unroll
         for (int pf = 0; pf < 2; ++pf) {
             const int f = kPF[wave][pf];
             if (f < 0) continue;
-            const int i = 16 * kFI[f] + l16;
-            const float gi = sG[i];
+            const int fI = kFI[f], i = 16 * fI + l16;
+            const float gi = sG[i], bi = sB[i];
             half8 v;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const int j0 = 16 * (2 * kFKS[f] + hh) + 4 * lq;
+                const int J = 2 * kFKS[f] + hh, j0 = 16 * J + 4 * lq;
+                if (J > fI) {  // above the diagonal (uniform): P is zero, L is never read
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[4 * hh + e] = static_cast<_Float16>(0.0f);
+                    continue;
+                }
                 const float4 gj = *reinterpret_cast<const float4 *>(sG + j0);
                 const float gjs[4] = {gj.x, gj.y, gj.z, gj.w};
+                float lv[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[4 * hh + e] = static_cast<_Float16>(keep_if_nonneg(i - (j0 + e), rawP[pf][hh][e] * hw_exp(gi - gjs[e])));
+                for (int e = 0; e < 4; ++e) {
+                    const float ex = hw_exp(gi - gjs[e]);
+                    v[4 * hh + e] = static_cast<_Float16>(keep_if_nonneg(i - (j0 + e), rawP[pf][hh][e] * ex));
+                    lv[e] = keep_if_nonneg(i - (j0 + e) - 1, bi * rawL[pf][hh][e] * ex);
+                }
+                *reinterpret_cast<float4 *>(sL + i * PL + j0) = make_float4(lv[0], lv[1], lv[2], lv[3]);
             }
             st_ws(rtp, (kPOff + f * kFrag) * 2 + lane * 16, v);
-        }
-        // L (fp32, strictly lower), rows i = 16 ti + 4 lq + e, column j = 16 tj + l16
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int tt = wave + 4 * u;
-            if (tt >= 10) continue;
-            int ti, tj;
-            tri_block(tt, ti, tj);
-            const int col = 16 * tj + l16, r0 = 16 * ti + 4 * lq;
-            const float gcol = sG[col];
-            const float4 gr = *reinterpret_cast<const float4 *>(sG + r0);
-            const float4 br = *reinterpret_cast<const float4 *>(sB + r0);
-            const float grs[4] = {gr.x, gr.y, gr.z, gr.w}, brs[4] = {br.x, br.y, br.z, br.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sL[(r0 + e) * PL + col] = keep_if_nonneg(r0 + e - 1 - col, brs[e] * rawL[u][e] * hw_exp(grs[e] - gcol));
         }
         lds_barrier();
 

@@ -42,10 +42,6 @@ constexpr int kTPF = kPOff + 6 * kFrag;
 
 __host__ __device__ constexpr int kpos(int m) { return m < 4 ? 8 * m : 8 * (m - 4) + 4; }
 
-__device__ __forceinline__ void tri_block(int blk, int &bi, int &bj) {
-    bi = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
-    bj = blk - bi * (bi + 1) / 2;
-}
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
