@@ -101,6 +101,19 @@ def test_prefill_ragged(T, Hk, Hv):
     _check_prefill(w)
 
 
+@pytest.mark.parametrize("B,T,Hk,Hv", [
+    (2, 150, 1, 16),  # 16 value heads per key head: the prep kernel's second pass over g and beta
+    (1, 130, 1, 40),  # 40 per key head: 56 KB of prep LDS, 40 chains in two-tile slices
+    (1, 200, 2, 64),  # 32 per key head on two key heads: the raised prep LDS limit (68 KB)
+])
+def test_prefill_many_value_heads_per_key_head(B, T, Hk, Hv):
+    """Head ratios past the eight value heads whose gates one pass of the prep kernel's 256
+    threads stages, and prep LDS past the default 64 KB limit, against the oracle."""
+    w = GI.Workload(f"wide_B{B}_T{T}_Hk{Hk}_Hv{Hv}", B, T, Hk, Hv, random_state=True, random_conv_state=True,
+                    tag=1900 + Hv)
+    _check_prefill(w)
+
+
 @pytest.mark.parametrize("conv,norm", [(False, True), (True, False), (False, False)])
 def test_prefill_conv_norm_switches(conv, norm):
     w = GI.Workload(f"switch_c{conv}_n{norm}", 1, 150, 2, 4, conv=conv, norm=norm, tag=400 + 2 * conv + norm)
