@@ -345,8 +345,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAXT <
                 const float kv = kn[rg + 16 * m], qv = qn[rg + 16 * m];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    pk[e] += S[m][e] * kv;
-                    pq[e] += S[m][e] * qv;
+                    pk[e] = __builtin_fmaf(S[m][e], kv, pk[e]);
+                    pq[e] = __builtin_fmaf(S[m][e], qv, pq[e]);
                 }
             }
 #pragma unroll
@@ -371,8 +371,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAXT <
                     PQ += sRed[(w * 2 + 1) * kD + j];
                 }
                 const float vj = sU[t * nu + 2 * kD + hr * kD + j];
-                const float d = sBe[hr * T + t] * (vj - alpha * PK);
-                oj = alpha * PQ + sQK[t] * d;
+                // fused multiply-adds in a fixed order here and in the update below, so that every
+                // instantiation (one step, several tokens) rounds alike
+                const float d = sBe[hr * T + t] * __builtin_fmaf(-alpha, PK, vj);
+                oj = __builtin_fmaf(sQK[t], d, alpha * PQ);
                 sD[j] = d;
                 if (a.norm) {
                     const float ss = wave_sum(oj * oj);
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MAXT <
                 const float kv = kn[rg + 16 * m];
                 floatx4 sv = S[m];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sv[e] = alpha * sv[e] + kv * d4[e];
+                for (int e = 0; e < 4; ++e) sv[e] = __builtin_fmaf(kv, d4[e], alpha * sv[e]);
                 S[m] = sv;
                 // The whole offset goes in the vector offset and the scalar offset is the constant
                 // 0: the compiler then models the hazard of a VALU write to the data registers of
