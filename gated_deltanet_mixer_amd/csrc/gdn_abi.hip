@@ -192,6 +192,10 @@ int prefill_impl(const gdn_shape *s, const int32_t *cu_seqlens, const uint16_t *
 
     PrefillPlan plan;
     plan_prefill(s->B, s->T, s->Hk, s->Hv, packed, s->prefill_segments, &plan);
+    // the static scratch: where the library's own choice of the two-level scan does not fit,
+    // the plain sequential pass (the smaller workspace) may
+    if (static_scratch && s->prefill_segments == 0 && plan.nseg > 1 && plan.total_bytes > kStaticScratchBytes)
+        plan_prefill(s->B, s->T, s->Hk, s->Hv, packed, 1, &plan);
     if (plan.nslots * s->Hk > 0x7fffffffLL) return GDN_EINVAL;
     if (workspace_bytes < plan.total_bytes) return GDN_EWORKSPACE;
     if (static_scratch && !(workspace = static_scratch_address())) return GDN_EHIP;

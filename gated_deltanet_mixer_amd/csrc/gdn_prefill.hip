@@ -1156,6 +1156,12 @@ struct ChainLaunch {
 // Two-level scan planning: the chip's compute units (MI355X) and the shortest segment.
 constexpr int kSegChipCUs = 256;
 constexpr int kSegMinChunks = 16;
+// Where the sequential pass would fill up to half of the chip (16-column slices of 9 to 16
+// chains), two segments fill all of it.  The segment pass runs half the chunks at a similar
+// pace per chunk, and the combine and output kernels add about 35 us, so the split pays from
+// about 64 chunks on.  0.8B-shaped layer (64 chunks, 16 chains): sequential pass 118 us against
+// segment pass 54 us + combine 17 us + outputs 19 us.
+constexpr int kSegMinChunksHalf = 32;
 
 // What a launch needs to know about a device and a kernel, found on first use and kept
 // (the queries cost tens of microseconds of host time per call otherwise).
@@ -1230,12 +1236,13 @@ int plan_prefill(int B, int T, int Hk, int Hv, bool packed, int segments, Prefil
     plan->xch_bytes = kHeaderBytes + plan->mbox_bytes;
     plan->qk_bytes = align256((size_t)plan->nslots * Hk * kQKF * sizeof(_Float16));
     plan->tp_bytes = align256((size_t)plan->nslots * Hv * kTPF * sizeof(_Float16));
-    // Two-level scan (even batches): worth it when the sequential pass would leave most of
-    // the chip idle (few heads) and the sequences are long.  Its first pass runs 256 columns
-    // per head in slices of 32 (measured on the shapes it is for: as many 32-column slices
-    // as fit the chip beat half as many segments in 16-column slices, at about 2 us against
-    // 1.25 us per chunk), so nseg segments keep B Hv 8 nseg workgroups busy; nseg fills one
-    // round of the chip.  `segments` overrides the choice (1: never, n >= 2: n segments).
+    // Two-level scan (even batches): worth it when the sequential pass would leave much of the
+    // chip idle (few heads) and the sequences are long.  Its first pass runs 256 columns per
+    // head in slices of 32 (measured on the shapes it is for: as many 32-column slices as fit
+    // the chip beat half as many segments in 16-column slices, at about 2 us against 1.25 us per
+    // chunk), so nseg segments keep B Hv 8 nseg workgroups busy; nseg fills one round of the
+    // chip (two segments where the sequential pass would fill half of it).  `segments`
+    // overrides the choice (1: never, n >= 2: n segments).
     plan->nseg = 1;
     plan->seg_chunks = plan->nchunks;
     if (!packed) {
@@ -1244,6 +1251,8 @@ int plan_prefill(int B, int T, int Hk, int Hv, bool packed, int segments, Prefil
             want = segments;
         else if (chains * nsl * 4 <= kSegChipCUs)  // the sequential pass would use at most a quarter of the chip
             want = std::min<long long>(kSegChipCUs / (chains * 8), plan->nchunks / kSegMinChunks);
+        else if (chains * 8 * 2 <= kSegChipCUs)  // at most half of it: two segments, if they are long
+            want = std::min<long long>(2, plan->nchunks / kSegMinChunksHalf);
         want = std::min<long long>(want, plan->nchunks);
         if (want >= 2) {
             plan->seg_chunks = (int)((plan->nchunks + want - 1) / want);

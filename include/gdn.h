@@ -171,7 +171,10 @@ int gdn_prefill_check(const void *workspace, size_t workspace_bytes, void *strea
  * once, on the first call with that device current, after the host checks.
  *
  * Arguments, layouts, results and errors are those of gdn_prefill (even
- * batches only).  A shape whose gdn_prefill_workspace_size exceeds
+ * batches only).  Where the library would choose the two-level scan
+ * (prefill_segments = 0) and its workspace does not fit
+ * GDN_STATIC_SCRATCH_BYTES, the call runs the plain sequential pass instead
+ * (the same results to rounding).  A shape whose workspace still exceeds
  * GDN_STATIC_SCRATCH_BYTES is rejected with GDN_EWORKSPACE before any HIP
  * call (the 0.8B-shaped layer, 16/16 heads, fits up to T = 8192 tokens).
  * Every call on one GPU uses the same array, which keeps the last call's

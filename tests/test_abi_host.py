@@ -278,12 +278,18 @@ def test_one_hip_runtime_per_process():
 
 def test_two_level_plan_sizes_the_workspace():
     """Few heads and a long sequence: the plan splits the sequence into segments, and the
-    workspace grows by their read-outs (32 KB per chunk and head) and segment maps.  The
-    benchmark shapes (16 or more heads) and packed batches keep the plain sequential pass."""
+    workspace grows by their read-outs (32 KB per chunk and head) and segment maps.  Up to 16
+    heads (whose sequential pass would fill at most half of the chip) take two segments from 64
+    chunks on, the 0.8B-shaped layer among them; the larger benchmark shapes, shorter sequences
+    of 16 heads and packed batches keep the plain sequential pass."""
     plain = gdn.gdn_prefill_workspace_size(_shape(B=1, T=262144, Hk=1, Hv=3, segments=1))
     planned = gdn.gdn_prefill_workspace_size(_shape(B=1, T=262144, Hk=1, Hv=3))
     assert planned - plain >= (262144 // 64) * 3 * 32 * 1024
-    for kw in (dict(B=1, T=4096, Hk=16, Hv=16), dict(B=4, T=16384, Hk=16, Hv=32),
+    plain = gdn.gdn_prefill_workspace_size(_shape(B=1, T=4096, Hk=16, Hv=16, segments=1))
+    planned = gdn.gdn_prefill_workspace_size(_shape(B=1, T=4096, Hk=16, Hv=16))
+    assert planned == gdn.gdn_prefill_workspace_size(_shape(B=1, T=4096, Hk=16, Hv=16, segments=2))
+    assert planned - plain >= 64 * 16 * 32 * 1024
+    for kw in (dict(B=1, T=4032, Hk=16, Hv=16), dict(B=1, T=65536, Hk=16, Hv=48), dict(B=4, T=16384, Hk=16, Hv=32),
                dict(B=3, T=65536, Hk=1, Hv=3, packed=True)):
         assert gdn.gdn_prefill_workspace_size(_shape(**kw)) == gdn.gdn_prefill_workspace_size(_shape(**kw, segments=1))
     # a forced split asks for more only when the sequence has more than one chunk

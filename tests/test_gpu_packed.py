@@ -105,13 +105,14 @@ def test_packed_many_sequences():
 
 
 def test_one_packed_sequence_equals_even_batch():
-    """B = 1 packed over T tokens is the even-batch call on the same tensors: bit-equal."""
+    """B = 1 packed over T tokens is the even-batch call on the same tensors: bit-equal (the even
+    batch held to the plain sequential pass, which packed sequences always take)."""
     R = _R()
     T, Hk, Hv = 4096, 16, 16
     w = GI.Workload("packed_one", 1, T, Hk, Hv, random_state=True, random_conv_state=True, tag=1310)
     inp = GI.make_inputs(w)
     print(f"[packed] one sequence T={T} {Hk}/{Hv}", flush=True)
-    even = R.Prefill(inp, 1, T, Hk, Hv, True, True)
+    even = R.Prefill(inp, 1, T, Hk, Hv, True, True, segments=1)
     even.run()
     pk = R.PackedPrefill(inp, [0, T], T, Hk, Hv, True, True, state_in=inp["state"], conv_state_in=inp["conv_state"])
     pk.run()

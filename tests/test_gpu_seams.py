@@ -136,12 +136,14 @@ def test_repeat_is_deterministic_and_state_may_alias():
     assert torch.equal(r.o, o1) and torch.equal(r.state_out, s1)
 
 
-def test_last_chunks_are_right_on_every_run():
-    """The sequential pass's load wave counts its outstanding loads to know when a DMA
-    group has landed; a count that is off by one near the end of a sequence lets the
-    gating read z rows that are still in flight, now and then.  Six runs of one shape,
-    each compared with the oracle on the last ten chunks and with the first run bit for
-    bit (a race shows up as run-to-run differences)."""
+@pytest.mark.parametrize("segments", [0, 1])
+def test_last_chunks_are_right_on_every_run(segments):
+    """The sequential pass's load wave (and the two-level scan's) counts its outstanding loads
+    to know when a DMA group has landed; a count that is off by one near the end of a sequence
+    lets the gating read z rows that are still in flight, now and then.  Six runs of one shape,
+    each compared with the oracle on the last ten chunks and with the first run bit for bit (a
+    race shows up as run-to-run differences); once as the library plans it (two segments on
+    this shape) and once held to the plain sequential pass."""
     R = _R()
     B, T, Hk, Hv = 1, 4096, 16, 16
     w = GI.Workload("tail_runs", B, T, Hk, Hv, random_state=True, random_conv_state=True, tag=704)
@@ -150,7 +152,7 @@ def test_last_chunks_are_right_on_every_run():
     t0 = T - 10 * 64
     first = None
     for i in range(6):
-        r = R.Prefill(inp, B, T, Hk, Hv, True, True)
+        r = R.Prefill(inp, B, T, Hk, Hv, True, True, segments=segments)
         r.run()
         torch.cuda.synchronize()
         assert r.exchange_error_word() == 0

@@ -66,6 +66,33 @@ def test_no_workspace_matches_workspace_call(B, T, Hk, Hv, states):
     np.testing.assert_array_equal(R.bits(cs_out), cs_ref)
 
 
+def test_no_workspace_falls_back_to_the_plain_pass():
+    """The 0.8B-shaped layer at T = 8192: the library plans the two-level scan, whose workspace
+    (about 190 MiB) exceeds the scratch, while the plain sequential pass's (about 120 MiB) fits.
+    The allocation-free call then runs the plain pass: bit-identical to gdn_prefill held to the
+    plain pass (prefill_segments = 1), and within the oracle's tolerance."""
+    R = _R()
+    import gated_deltanet_mixer_amd as gdn
+    B, T, Hk, Hv = 1, 8192, 16, 16
+    assert gdn.gdn_prefill_workspace_size(gdn.make_shape(B, T, Hk, Hv)) > gdn.GDN_STATIC_SCRATCH_BYTES
+    assert gdn.gdn_prefill_workspace_size(gdn.make_shape(B, T, Hk, Hv, segments=1)) <= gdn.GDN_STATIC_SCRATCH_BYTES
+    w = GI.Workload("noalloc_fallback", B, T, Hk, Hv, random_state=True, random_conv_state=True, tag=1830)
+    inp = GI.make_inputs(w)
+    print(f"[no_alloc] fallback B={B} T={T} {Hk}/{Hv}", flush=True)
+    run = R.Prefill(inp, B, T, Hk, Hv, True, True, segments=1)
+    run.run()
+    # the library's own plan choice (prefill_segments = 0), not the plain-pass shape of `run`
+    o = torch.full_like(run.o, 0x7fc0)
+    state_out = torch.full_like(run.state_out, float("nan"))
+    cs_out = torch.full_like(run.conv_state_out, 0x7fc0)
+    d = run.d
+    gdn.gdn_prefill_no_workspace(gdn.make_shape(B, T, Hk, Hv), d["q"], d["k"], d["v"], d["g"], d["beta"], d["z"],
+                                 d["conv_w"], d["norm_w"], d["state_in"], d["conv_state_in"], o, state_out, cs_out)
+    torch.cuda.synchronize()
+    assert run.exchange_error_word() == 0
+    assert torch.equal(o, run.o) and torch.equal(state_out, run.state_out) and torch.equal(cs_out, run.conv_state_out)
+
+
 def test_no_workspace_rejects_shapes_beyond_the_scratch():
     """A well-formed call whose workspace would exceed the scratch is rejected by a host check,
     before any HIP call (disjoint fake device addresses, never dereferenced)."""
