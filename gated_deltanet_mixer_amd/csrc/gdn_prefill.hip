@@ -1027,6 +1027,7 @@ struct SegArgs {
     const uint16_t *z, *norm_w;
     uint16_t *o;
     int B, T, Hv, nch, nseg, seg_chunks, norm;
+    int out_cpw;             // chunks per workgroup of the output kernel (consecutive, one segment)
     float eps_norm;
 };
 
@@ -1034,20 +1035,47 @@ struct SegArgs {
 // S_{p+1} = M_p S_p + N_p (each segment's map is affine in its start state).  One
 // workgroup per (head, 16-column slice): the columns of a state never mix.  The start
 // state of every segment is also written as MFMA operand fragments for the output pass.
-// grid (B Hv 8), 256 threads
-__global__ __launch_bounds__(256) void seg_combine_kernel(SegArgs a) {
+// The products run on the fp32 MFMA (16x16x4): wave w owns rows 16 w .. 16 w + 15, and its
+// lane l (row i = l % 16, quarter q = l / 16) brings the k-steps s = 0..31 of the contraction
+// index k = 32 q + s, so that its A values are one contiguous piece of row 16 w + i of M.
+// Two register sets hold those pieces (and the lane's N values) of segments p and p + 1; each
+// is reloaded with segment p + 2 right after its last use, so the chain of segments waits on
+// memory once.  Two accumulators split the 32 k-steps into independent MFMA chains.
+// grid (B Hv 8), 512 threads
+__global__ __launch_bounds__(512) void seg_combine_kernel(SegArgs a) {
     __shared__ float sS[kD][16 + 1];
     const int chain = blockIdx.x / kTiles, ct = blockIdx.x % kTiles;
-    const int tid = threadIdx.x;
-    for (int i = tid; i < kD * 16; i += 256) {
-        const int r = i / 16, j = i % 16;
-        sS[r][j] = a.state_in ? a.state_in[((size_t)chain * kD + r) * kD + 16 * ct + j] : 0.0f;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, i = lane & 15, q = lane >> 4;
+    auto mrow = [&](int p, int row) { return a.seg_state + (((size_t)chain * a.nseg + p) * kD + row) * (2 * kD); };
+    // M[16 w + i][32 q .. 32 q + 31] and N[16 w + 4 q + v][16 ct + i] of segment p (clamped)
+    auto fetch = [&](int p, float4 (&m)[8], float (&n)[4]) __attribute__((always_inline)) {
+        const int pc = min(p, a.nseg - 1);
+        const float *M = mrow(pc, 16 * w + i) + 32 * q;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m[u] = *reinterpret_cast<const float4 *>(M + 4 * u);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) n[v] = mrow(pc, 16 * w + 4 * q + v)[kD + 16 * ct + i];
+    };
+    // the start state first (the first step waits for it alone), then both register sets
+    float s0[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int x = tid + 512 * e, rr = x / 16, j = x % 16;
+        s0[e] = a.state_in ? a.state_in[((size_t)chain * kD + rr) * kD + 16 * ct + j] : 0.0f;
+    }
+    float4 mA[8], mB[8];
+    float nA[4], nB[4];
+    fetch(0, mA, nA);
+    fetch(1, mB, nB);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int x = tid + 512 * e;
+        sS[x / 16][x % 16] = s0[e];
     }
     __syncthreads();
-    const int r = tid >> 1, j0 = (tid & 1) * 8;  // this thread's row and 8 columns
-    for (int p = 0; p < a.nseg; ++p) {
+    auto step = [&](int p, float4 (&m)[8], float (&n)[4]) __attribute__((always_inline)) {
         const size_t vc = (size_t)chain * a.nseg + p;
-        {   // fragment ks of column tile ct: lane L holds column l16 at rows 32 ks + {4 lq + e, 16 + 4 lq + e}
+        if (tid < 256) {  // fragment ks of column tile ct: lane L holds column l16 at rows 32 ks + {4 lq + e, 16 + 4 lq + e}
             const int ks = tid >> 6, L = tid & 63, l16 = L & 15, lq = L >> 4;
             half8 f;
 #pragma unroll
@@ -1057,92 +1085,144 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(SegArgs a) {
             }
             *reinterpret_cast<half8 *>(a.seg_frag + (((vc * kTiles + ct) * 4 + ks) * 64 + L) * 8) = f;
         }
-        const float *Mrow = a.seg_state + (vc * kD + r) * (2 * kD);
-        float acc[8];
+        // D rows 16 w + 4 q + v, column i: N plus the two chains
+        floatx4 acc0 = {n[0], n[1], n[2], n[3]}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = Mrow[kD + 16 * ct + j0 + j];
-        for (int k = 0; k < kD; k += 4) {
-            const float4 m = *reinterpret_cast<const float4 *>(Mrow + k);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[j] += m.x * sS[k][j0 + j] + m.y * sS[k + 1][j0 + j] + m.z * sS[k + 2][j0 + j] + m.w * sS[k + 3][j0 + j];
+        for (int u = 0; u < 8; u += 2) {
+            const int k = 32 * q + 4 * u;
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u].x, sS[k][i], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u + 1].x, sS[k + 4][i], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u].y, sS[k + 1][i], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u + 1].y, sS[k + 5][i], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u].z, sS[k + 2][i], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u + 1].z, sS[k + 6][i], acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u].w, sS[k + 3][i], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(m[u + 1].w, sS[k + 7][i], acc1, 0, 0, 0);
         }
+        fetch(p + 2, m, n);  // this set's next segment, past the last use
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sS[r][j0 + j] = acc[j];
+        for (int v = 0; v < 4; ++v) sS[16 * w + 4 * q + v][i] = acc0[v] + acc1[v];
         __syncthreads();
+    };
+    for (int p = 0; p < a.nseg; p += 2) {
+        step(p, mA, nA);
+        if (p + 1 < a.nseg) step(p + 1, mB, nB);
     }
-    for (int i = tid; i < kD * 16; i += 256) {
-        const int rr = i / 16, jj = i % 16;
+    for (int x = tid; x < kD * 16; x += 512) {
+        const int rr = x / 16, jj = x % 16;
         a.state_out[((size_t)chain * kD + rr) * kD + 16 * ct + jj] = sS[rr][jj];
     }
 }
 
 // Outputs of the two-level scan: O = O0 + R S_p for chunk c of segment p (R [64][128]
-// times the start state, on MFMA), then the gated RMSNorm and the bf16 store.  Wave w
-// owns rows 16 w .. 16 w + 15 of the chunk; a row's 128 columns sit in 16 lanes.  O0, z
-// and the outputs pass through LDS so that every global access is a 16-byte row piece.
-// grid (B nch Hv), 256 threads
+// times the start state, on MFMA), then the gated RMSNorm and the bf16 store.  A workgroup
+// takes out_cpw consecutive chunks of one segment and head and keeps the segment's start
+// state (32 B-operand fragments, 32 KB) in LDS across them; the next chunk's R, O0 and z are
+// in flight while one is computed.  Wave w owns rows 16 w .. 16 w + 15 of a
+// chunk; a row's 128 columns sit in 16 lanes.  O0, z and the outputs pass through LDS so
+// that every global access is a 16-byte row piece.
+// grid (B Hv nseg pieces), 256 threads
 __global__ __launch_bounds__(256) void seg_output_kernel(SegArgs a) {
     __shared__ _Float16 sX[kC][kD + 8];  // O0, then the bf16 outputs
     __shared__ uint16_t sZ[kC][kD + 8];  // z
-    const int gc = blockIdx.x / a.Hv, h = blockIdx.x % a.Hv;
-    const int b = gc / a.nch, c = gc % a.nch, p = c / a.seg_chunks;
+    __shared__ half8 sF[32][64];         // start-state fragment (column tile ct, k-step ks) at 4 ct + ks
+    const int npiece = (a.seg_chunks + a.out_cpw - 1) / a.out_cpw;
+    int id = blockIdx.x;
+    const int piece = id % npiece;
+    id /= npiece;
+    const int p = id % a.nseg;
+    id /= a.nseg;
+    const int h = id % a.Hv, b = id / a.Hv;
+    const int c_begin = p * a.seg_chunks + piece * a.out_cpw;
+    const int c_end = min(min(c_begin + a.out_cpw, (p + 1) * a.seg_chunks), a.nch);
+    if (c_begin >= c_end) return;  // the last segment is shorter (uniform over the workgroup)
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, lq = lane >> 4;
     const size_t vc = ((size_t)b * a.Hv + h) * a.nseg + p;
-    const size_t row0 = (size_t)b * a.T + (size_t)c * kC;
-    const int nrows = min(kC, a.T - c * kC);
-    const _Float16 *blk = a.seg_out + ((size_t)gc * a.Hv + h) * kSegBlk;
-    for (int i = tid; i < kC * 16; i += 256) {
-        const int row = i >> 4, c8 = (i & 15) * 8;
-        *reinterpret_cast<half8 *>(&sX[row][c8]) = *reinterpret_cast<const half8 *>(blk + kSegR + row * kD + c8);
-        if (a.norm)
-            *reinterpret_cast<uint4 *>(&sZ[row][c8]) =
-                row < nrows ? *reinterpret_cast<const uint4 *>(a.z + ((row0 + row) * a.Hv + h) * kD + c8)
-                            : make_uint4(0, 0, 0, 0);
+    {
+        const half8 *fr = reinterpret_cast<const half8 *>(a.seg_frag) + vc * kTiles * 4 * 64;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sF[8 * w + u][lane] = fr[(8 * w + u) * 64 + lane];
     }
-    half8 A[4];
+    // the chunk's O0 rows and z rows of this thread (4 pieces each) and its wave's R fragments:
+    // once chunk c's are in LDS (and R in named registers), the set is reloaded with chunk c + 1
+    // (past the last chunk, the last one's again), in flight while chunk c is computed
+    uint4 oP[4], zP[4], aP[4];
+    auto load_chunk = [&](int c, uint4 (&xo)[4], uint4 (&xz)[4], uint4 (&xa)[4]) __attribute__((always_inline)) {
+        const size_t gc = (size_t)b * a.nch + c, row0 = (size_t)b * a.T + (size_t)c * kC;
+        const int nrows = min(kC, a.T - c * kC);
+        const _Float16 *blk = a.seg_out + (gc * a.Hv + h) * kSegBlk;
+        // z rows through a buffer resource over the chunk's rows: rows past T (and every row
+        // without the norm, where z is absent) read as zero, with no branch around the loads
+        const __amdgpu_buffer_rsrc_t rz =
+            make_rsrc(a.norm ? a.z + (row0 * a.Hv + h) * kD : a.o, a.norm ? (unsigned int)nrows * a.Hv * kD * 2 : 0u);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(blk, kSegBlk * 2);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) A[ks] = *reinterpret_cast<const half8 *>(blk + ((w * 4 + ks) * 64 + lane) * 8);
-    floatx4 acc[8];
-    const half8 *fr = reinterpret_cast<const half8 *>(a.seg_frag) + vc * kTiles * 4 * 64 + lane;
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + 256 * u, row = i >> 4, c8 = (i & 15) * 8;
+            xo[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, (kSegR + row * kD + c8) * 2, 0, 0));
+            xz[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rz, (row * a.Hv * kD + c8) * 2, 0, 0));
+        }
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-        acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 4; ++ks)
+            xa[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, ((w * 4 + ks) * 64 + lane) * 16, 0, 0));
+    };
+    auto do_chunk = [&](int c, uint4 (&xo)[4], uint4 (&xz)[4], uint4 (&xa)[4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc[ct] = mfma16x16x32(A[ks], fr[(ct * 4 + ks) * 64], acc[ct]);
-    }
-    __syncthreads();
-    float ss[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int row = 16 * w + 4 * lq + e;
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + 256 * u, row = i >> 4, c8 = (i & 15) * 8;
+            *reinterpret_cast<uint4 *>(&sX[row][c8]) = xo[u];
+            *reinterpret_cast<uint4 *>(&sZ[row][c8]) = xz[u];
+        }
+        const half8 A0 = __builtin_bit_cast(half8, xa[0]), A1 = __builtin_bit_cast(half8, xa[1]),
+                    A2 = __builtin_bit_cast(half8, xa[2]), A3 = __builtin_bit_cast(half8, xa[3]);
+        load_chunk(min(c + 1, c_end - 1), xo, xz, xa);
+        __syncthreads();
+        floatx4 acc[8];
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            acc[ct][e] += (float)sX[row][16 * ct + l16];
-            ss[e] += acc[ct][e] * acc[ct][e];
+            acc[ct] = mfma16x16x32(A0, sF[4 * ct][lane], floatx4{0.f, 0.f, 0.f, 0.f});
+            acc[ct] = mfma16x16x32(A1, sF[4 * ct + 1][lane], acc[ct]);
+            acc[ct] = mfma16x16x32(A2, sF[4 * ct + 2][lane], acc[ct]);
+            acc[ct] = mfma16x16x32(A3, sF[4 * ct + 3][lane], acc[ct]);
         }
-    }
-    __syncthreads();  // sX is reused for the outputs
+        float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int row = 16 * w + 4 * lq + e;
-        const float rstd = __builtin_amdgcn_rsqf(row16_sum(ss[e]) * (1.0f / kD) + a.eps_norm);
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * w + 4 * lq + e;
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int col = 16 * ct + l16;
-            float y = acc[ct][e];
-            if (a.norm) y = bf16_to_f32(a.norm_w[col]) * (y * rstd) * silu(bf16_to_f32(sZ[row][col]));
-            reinterpret_cast<uint16_t *>(&sX[row][0])[col] = f32_to_bf16(y);
+            for (int ct = 0; ct < 8; ++ct) {
+                acc[ct][e] += (float)sX[row][16 * ct + l16];
+                ss[e] += acc[ct][e] * acc[ct][e];
+            }
         }
-    }
-    __syncthreads();
-    for (int i = tid; i < kC * 16; i += 256) {
-        const int row = i >> 4, c8 = (i & 15) * 8;
-        if (row < nrows)
-            *reinterpret_cast<uint4 *>(a.o + ((row0 + row) * a.Hv + h) * kD + c8) =
-                *reinterpret_cast<const uint4 *>(&sX[row][c8]);
-    }
+        __syncthreads();  // sX is reused for the outputs
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * w + 4 * lq + e;
+            const float rstd = __builtin_amdgcn_rsqf(row16_sum(ss[e]) * (1.0f / kD) + a.eps_norm);
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const int col = 16 * ct + l16;
+                float y = acc[ct][e];
+                if (a.norm) y = bf16_to_f32(a.norm_w[col]) * (y * rstd) * silu(bf16_to_f32(sZ[row][col]));
+                reinterpret_cast<uint16_t *>(&sX[row][0])[col] = f32_to_bf16(y);
+            }
+        }
+        __syncthreads();
+        const size_t row0 = (size_t)b * a.T + (size_t)c * kC;
+        const int nrows = min(kC, a.T - c * kC);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + 256 * u, row = i >> 4, c8 = (i & 15) * 8;
+            if (row < nrows)
+                *reinterpret_cast<uint4 *>(a.o + ((row0 + row) * a.Hv + h) * kD + c8) =
+                    *reinterpret_cast<const uint4 *>(&sX[row][c8]);
+        }
+        __syncthreads();  // the next chunk's O0 and z overwrite sX and sZ
+    };
+    load_chunk(c_begin, oP, zP, aP);
+    for (int c = c_begin; c < c_end; ++c) do_chunk(c, oP, zP, aP);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1158,9 +1238,9 @@ constexpr int kSegChipCUs = 256;
 constexpr int kSegMinChunks = 16;
 // Where the sequential pass would fill up to half of the chip (16-column slices of 9 to 16
 // chains), two segments fill all of it.  The segment pass runs half the chunks at a similar
-// pace per chunk, and the combine and output kernels add about 35 us, so the split pays from
+// pace per chunk, and the combine and output kernels add about 30 us, so the split pays from
 // about 64 chunks on.  0.8B-shaped layer (64 chunks, 16 chains): sequential pass 118 us against
-// segment pass 54 us + combine 17 us + outputs 19 us.
+// segment pass 54 us + combine 11 us + outputs 21 us.
 constexpr int kSegMinChunksHalf = 32;
 
 // What a launch needs to know about a device and a kernel, found on first use and kept
@@ -1350,12 +1430,16 @@ int launch_prefill(const PrefillParams &p, const PrefillPlan &plan, hipStream_t 
     sa.state_out = p.state_out; sa.seg_out = a.seg_out; sa.z = p.z; sa.norm_w = p.norm_w; sa.o = p.o;
     sa.B = p.B; sa.T = p.T; sa.Hv = p.Hv; sa.nch = plan.nchunks; sa.nseg = plan.nseg;
     sa.seg_chunks = plan.seg_chunks; sa.norm = p.norm; sa.eps_norm = p.eps_norm;
+    // output workgroups: up to 8 chunks each, while at least two per CU of the chip remain
+    const long long chunk_heads = (long long)chains * plan.nseg * plan.seg_chunks;
+    sa.out_cpw = (int)std::max<long long>(1, std::min<long long>(8, chunk_heads / (2 * kSegChipCUs)));
+    const long long out_grid = (long long)chains * plan.nseg * ((plan.seg_chunks + sa.out_cpw - 1) / sa.out_cpw);
     void *sargs[] = {&sa};
     if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_combine_kernel), dim3((unsigned)(chains * kTiles)),
-                             dim3(256), sargs, 0, stream)) != hipSuccess)
+                             dim3(512), sargs, 0, stream)) != hipSuccess)
         return fail("hipLaunchKernel(seg_combine_kernel)", e);
-    if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_output_kernel),
-                             dim3((unsigned)((size_t)p.B * plan.nchunks * p.Hv)), dim3(256), sargs, 0, stream)) !=
+    if ((e = hipLaunchKernel(reinterpret_cast<const void *>(seg_output_kernel), dim3((unsigned)out_grid), dim3(256),
+                             sargs, 0, stream)) !=
         hipSuccess)
         return fail("hipLaunchKernel(seg_output_kernel)", e);
     return 0;
