@@ -57,6 +57,8 @@ def _run_and_check(R, inp, B, T, Hk, Hv, conv, norm, nseg, label):
     (1, 327, 1, 1, False, False, 3),     # raw path
     (3, 200, 4, 12, True, True, 2),      # 36 heads: the 32-column slicing of the first pass
     (1, 4096, 1, 3, True, True, None),   # the library's own choice for few heads and a long sequence
+    (3, 4100, 1, 3, True, True, None),   # 9 chains: two segments by the plan's own choice, the last one
+                                         # a chunk shorter and ragged (65 chunks)
 ])
 def test_segment_parallel_prefill(B, T, Hk, Hv, conv, norm, nseg):
     R = _R()
