@@ -70,21 +70,12 @@ struct PassLds {
     static constexpr int BV = 16 * NT;              // value columns of the slice
     static constexpr int VT = BV * PL;              // floats of one column-major [BV][PL] output tile
     static constexpr int NRD = kC * BV * 2 / 1024;  // DMA instructions for 64 raw v rows of the slice
-    // Column j of conv(v) starts at fp16 offset vcol(j): a 136-byte stride puts the 16 columns
-    // that one X read covers (8 bytes per lane) on distinct LDS banks, and the 16-byte shift of
-    // columns 16..31 does the same for a conv store's 32 lanes (8 column groups x 4 row pairs).
-    static constexpr int SV = kC + 4;
-    static constexpr int SVT = BV * SV + 8;  // one buffer
-    static __device__ __forceinline__ constexpr int vcol(int j) { return j * SV + 8 * ((j >> 4) & 1); }
-    // Pre-norm output: row i of column j sits at position (i + ROT (j / 8)) mod 64 of the
-    // column.  A gating read takes one row of 8-column groups from 64 / (8 NCG) rows per
-    // half-wave; without the rotation every group of a row falls on one bank.
-    static constexpr int ROT = 256 / BV;
+    static constexpr int SVT = vtile(BV);           // fp16 of one conv(v) buffer
     static constexpr size_t sK = 0;                                // [3][16 KB] k^ fragments
     static constexpr size_t sTB = sK + 3 * 16 * 1024;              // [3][kTB]   T diag(beta) fragments, decays
     static constexpr size_t sSD = sTB + 3 * kTB;                   // [2][NT][kSDT] Sb, Delta per tile
-    static constexpr size_t sV = sSD + 2 * NT * kSDT;              // fp16 [2][SVT] conv(v), column-major
-    static constexpr size_t sO = sV + 2 * 2 * SVT;                 // fp32 [kORingP][BV][PL] pre-norm output, rotated rows
+    static constexpr size_t sV = sSD + 2 * NT * kSDT;              // fp16 [2][SVT] conv(v), columns at vcol
+    static constexpr size_t sO = sV + 2 * 2 * SVT;                 // fp32 [kORingP][BV][PL] pre-norm output, rows at orow
     static constexpr size_t sRawV = sO + 4 * kORingP * VT;         // bf16 [3][64][BV] raw v
     static constexpr size_t sHalo = sRawV + 2 * 3 * kC * BV;       // bf16 [2][3][BV] raw v rows before a chunk
     static constexpr size_t sRstd = sHalo + 2 * 2 * 3 * BV;        // fp32 [2][64] 1/rms
@@ -149,7 +140,7 @@ __device__ __forceinline__ void state_chunk(const unsigned char *smem, floatx4 (
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const float4 eg = dec[4 * I + lq];
-            const half4 vv = lds_half4(sVc + L::vcol(16 * t + l16) + 16 * I + 4 * lq);
+            const half4 vv = lds_half4(sVc + vcol(16 * t + l16) + 16 * I + 4 * lq);
             X[I][0] = (float)vv[0] - eg.x * ks[I][t][0];
             X[I][1] = (float)vv[1] - eg.y * ks[I][t][1];
             X[I][2] = (float)vv[2] - eg.z * ks[I][t][2];
@@ -261,8 +252,8 @@ __device__ __forceinline__ void readout_chunk(unsigned char *smem, half8 (&fq)[1
                 ot = mfma16x16x32(fp[2 + 2 * (I - 2)], Db[t][0], ot);
                 ot = mfma16x16x32(fp[3 + 2 * (I - 2)], Db[t][1], ot);
             }
-            const int row = (16 * I + 4 * lq + ((16 * t + l16) >> 3) * L::ROT) & (kC - 1);
-            *reinterpret_cast<float4 *>(sOc + (16 * t + l16) * PL + row) = make_float4(ot[0], ot[1], ot[2], ot[3]);
+            const int j = 16 * t + l16;
+            *reinterpret_cast<float4 *>(sOc + j * PL + orow(L::BV, 16 * I + 4 * lq, j)) = make_float4(ot[0], ot[1], ot[2], ot[3]);
         }
     }
 #pragma unroll
@@ -506,7 +497,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     x[j][2] = __uint_as_float(rw[j].y << 16);
                     x[j][3] = __uint_as_float(rw[j].y & 0xffff0000u);
                 }
-                _Float16 *dst = sV + (cc & 1) * L::SVT + L::vcol(c4 * 4) + r0;  // columns 4 c4 .. 4 c4 + 3
+                _Float16 *dst = sV + (cc & 1) * L::SVT + vcol(c4 * 4) + r0;  // columns 4 c4 .. 4 c4 + 3
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float u[RPI];
@@ -519,7 +510,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         const float sil = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(acc * -1.4426950408889634f));
                         u[i] = bit_select(conv_mask, sil, x[i + 3][e]);
                     }
-                    *reinterpret_cast<halfx2 *>(dst + e * L::SV) = halfx2{static_cast<_Float16>(u[0]), static_cast<_Float16>(u[1])};
+                    *reinterpret_cast<halfx2 *>(dst + e * kVStride) = halfx2{static_cast<_Float16>(u[0]), static_cast<_Float16>(u[1])};
                 }
             };
             lds_barrier();  // taps, weights and halo staged; DMA groups 0, 1 landed
@@ -539,7 +530,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 unsigned long long mA[NSL], mB[NSL];
                 int xrow[NCG];  // position of row `lane` in each 8-column group's columns
 #pragma unroll
-                for (int g = 0; g < NCG; ++g) xrow[g] = (lane + g * L::ROT) & (kC - 1);
+                for (int g = 0; g < NCG; ++g) xrow[g] = orow(BV, lane, 8 * g);
                 auto mb_request = [&](int cc, unsigned long long(&m)[NSL]) __attribute__((always_inline)) {
                     const int ccl = min(max(cc, 0), nch - 1);
 #pragma unroll
@@ -627,7 +618,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int u = 0; u < GPL; ++u) {
                     const int it = gl + 64 * NGT * u, row = it < NGATE ? it / NCG : kC;  // row kC: past every resource
                     voff[u] = ((row * a.Hv + h) * kD + sv0 + cg8[u] * 8) * 2;
-                    grow[u] = ((it < NGATE ? row : 0) + cg8[u] * L::ROT) & (kC - 1);
+                    grow[u] = orow(BV, it < NGATE ? row : 0, 8 * cg8[u]);
                 }
                 auto z_load = [&](int oc, uint4(&z)[GPL]) __attribute__((always_inline)) {
                     const __amdgpu_buffer_rsrc_t rz = rows_rsrc(zsrc, oc);

@@ -73,7 +73,7 @@ struct PrepLds {
     static constexpr size_t sL = 0;                        // fp32 [64][PL]    (per value head from here on)
     static constexpr size_t sTd = sL + 4 * kC * PL;        // fp32 [4][16][PTD]
     static constexpr size_t sT16T = sTd + 4 * 4 * 16 * PTD;  // fp16 [64][P64]  T transposed
-    static constexpr size_t sTbst = sT16T + 2 * kC * P64;  // fp16 [10][256]  T diag(beta) staging
+    static constexpr size_t sTbst = sT16T + 2 * kC * P64;  // fp16 [10][16][kTBS] T diag(beta) staging
     static constexpr size_t sGr = sTbst + 2 * 10 * kBlk;   // fp32 [r][64] g (then G), then [r][64] beta, of every value head
     static_assert(sGr >= sK + 2 * kC * P128, "g/beta staging must not overlay q^/k^");
     static size_t bytes(int r) { return sGr + 2 * 4 * (size_t)kC * r; }
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int rr = 0; rr < 16; ++rr) {
                 sTd[(blk * 16 + rr) * PTD + cidx] = x[rr];
                 sT16T[(w0 + cidx) * P64 + w0 + rr] = static_cast<_Float16>(x[rr]);
-                sTbst[db * kBlk + rr * 16 + cidx] = static_cast<_Float16>(x[rr] * bc);
+                sTbst[db * kBlk + rr * kTBS + cidx] = static_cast<_Float16>(x[rr] * bc);
             }
         }
         lds_barrier();
@@ -412,20 +412,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int I = J + 1; I < 4; ++I) {
                 floatx4 y = {0.f, 0.f, 0.f, 0.f};
                 for (int K = J; K < I; ++K) {
-                    half4 av;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        av[e] = static_cast<_Float16>(sL[(16 * I + l16) * PL + 16 * K + 4 * lq + e]);
+                    // one 16-byte read per lane (four 4-byte reads of it put two lanes on a bank)
+                    const float4 l4 = *reinterpret_cast<const float4 *>(sL + (16 * I + l16) * PL + 16 * K + 4 * lq);
+                    const half4 av = {static_cast<_Float16>(l4.x), static_cast<_Float16>(l4.y),
+                                      static_cast<_Float16>(l4.z), static_cast<_Float16>(l4.w)};
                     const half4 bv = lds_half4(sT16T + (16 * J + l16) * P64 + 16 * K + 4 * lq);
                     y = mfma16x16x16(av, bv, y);
                 }
                 // y's accumulator layout is the B-operand layout of the next product
-                half4 yb, tv;
+                half4 yb;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    yb[e] = static_cast<_Float16>(y[e]);
-                    tv[e] = static_cast<_Float16>(sTd[(I * 16 + l16) * PTD + 4 * lq + e]);
-                }
+                for (int e = 0; e < 4; ++e) yb[e] = static_cast<_Float16>(y[e]);
+                const float4 t4 = *reinterpret_cast<const float4 *>(sTd + (I * 16 + l16) * PTD + 4 * lq);
+                const half4 tv = {static_cast<_Float16>(t4.x), static_cast<_Float16>(t4.y),
+                                  static_cast<_Float16>(t4.z), static_cast<_Float16>(t4.w)};
                 floatx4 t = {0.f, 0.f, 0.f, 0.f};
                 t = mfma16x16x16(tv, yb, t);
                 half4 th;
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     th[e] = static_cast<_Float16>(-t[e]);
-                    sTbst[blk * kBlk + (4 * lq + e) * 16 + l16] = static_cast<_Float16>(-t[e] * bcol);
+                    sTbst[blk * kBlk + (4 * lq + e) * kTBS + l16] = static_cast<_Float16>(-t[e] * bcol);
                 }
                 *reinterpret_cast<half4 *>(sT16T + (16 * J + l16) * P64 + 16 * I + 4 * lq) = th;
                 wave_lds_sync();
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             for (int hh = 0; hh < 2; ++hh) {
                 const int bj = 2 * ks + hh;  // the 16-column block of these 4 columns
                 half4 q4 = {0, 0, 0, 0};
-                if (bj <= bi) q4 = lds_half4(sTbst + (bi * (bi + 1) / 2 + bj) * kBlk + fl * 16 + 4 * fq);
+                if (bj <= bi) q4 = lds_half4(sTbst + (bi * (bi + 1) / 2 + bj) * kBlk + fl * kTBS + 4 * fq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[4 * hh + e] = q4[e];
             }

@@ -18,6 +18,22 @@ constexpr int P64 = kC + 8;    // fp16 rows of 64
 constexpr int PL = kC + 4;     // fp32 rows of 64
 constexpr int PTD = 20;        // fp32 rows of a 16x16 block
 
+// conv(v) of a slice in the sequential pass, fp16 column-major: column j starts at
+// vcol(j).  The 136-byte stride puts the 16 columns that one X read covers (8 bytes per
+// lane) on distinct LDS banks; the 16-byte shift of columns 16..31 does the same for the
+// lanes of a conv store, 8 column groups by the row groups of a half-wave.  (The segment
+// pass keeps P64 columns and plain output rows: there the same change measured no gain.)
+constexpr int kVStride = kC + 4;
+__host__ __device__ constexpr int vcol(int j) { return j * kVStride + 8 * ((j >> 4) & 1); }
+__host__ __device__ constexpr int vtile(int bv) { return bv * kVStride + 8; }  // fp16 of one buffer
+// Pre-norm output ring of the sequential pass, fp32 column-major [bv][PL]: row i of column j sits
+// at orow(bv, i, j).  The gating lanes read one 8-column group of one row each, a half-wave
+// covering 256 / bv consecutive rows; unrotated, the groups of a row fall on one bank, rotated
+// by 256 / bv rows per group they fill all 32.  Rows 4 m .. 4 m + 3 stay together, so a float4
+// of 4 rows is still one 16-byte store.
+__host__ __device__ constexpr int orot(int bv) { return 256 / bv; }
+__host__ __device__ constexpr int orow(int bv, int i, int j) { return (i + (j >> 3) * orot(bv)) & (kC - 1); }
+
 // Workspace blocks (fp16 elements), written by the prep kernel as MFMA operand
 // fragments: fragment f holds, for lane L = l16 + 16 lq, the 8 values of row
 // (tile row) + l16 at contraction indices 32 ks + {4 lq .. 4 lq + 3} and
@@ -31,7 +47,9 @@ constexpr int PTD = 20;        // fp32 rows of a 16x16 block
 //                                           only the blocks that are not all zero), fp32
 //                                           e^{G_i} [64], e^{G_C - G_i} [64], e^{G_C} [4]
 //                                           (1 KB), then P = (Q K^T) o R f = 0..5
-constexpr int kBlk = 256;                              // one 16x16 block (prep staging)
+constexpr int kTBS = 20;                               // fp16 row pitch of a staged 16x16 block: the 16 rows
+                                                       // of one 8-byte fragment read fall on distinct banks
+constexpr int kBlk = 16 * kTBS;                        // one staged 16x16 block (prep)
 constexpr int kFrag = 64 * 8;                          // one fragment: 64 lanes x 8 fp16
 constexpr int kQKF = 48 * kFrag;
 constexpr int kKOff = 16 * kFrag;                      // k^ fragments inside a q/k block
