@@ -111,9 +111,11 @@ __device__ __forceinline__ void state_chunk(const unsigned char *smem, floatx4 (
 #pragma unroll
         for (int f = 0; f < 6; ++f) tbf[f] = *reinterpret_cast<const half8 *>(tb + f * 1024 + lane * 16);
     }
-    // K S over the four 32-key steps.  The LDS stores of the chunk (S before the chunk and
-    // Delta, for the read-out wave) all come after the chunk's last LDS read: LDS operations
-    // complete in order, so a read issued after a store would wait for that store too.
+    // K S over the four 32-key steps.  Each step's fp16 S fragments go to LDS for the read-out
+    // wave as soon as they are packed, so they are packed once.  LDS operations complete in
+    // order, so the next step's k^ reads queue behind these stores; measured, that costs less
+    // than packing S a second time after the chunk's last read (27B-shaped pass, median
+    // 6.49 against 6.55 ms).  Delta goes to LDS after the chunk's last read.
     floatx4 ks[4][NT];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
@@ -126,7 +128,10 @@ __device__ __forceinline__ void state_chunk(const unsigned char *smem, floatx4 (
         for (int I = 0; I < 4; ++I) a[I] = *reinterpret_cast<const half8 *>(kb + (4 * I + s2) * 1024);
         half8 sb[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) sb[t] = pack_tiles(S[t][2 * s2], S[t][2 * s2 + 1]);
+        for (int t = 0; t < NT; ++t) {
+            sb[t] = pack_tiles(S[t][2 * s2], S[t][2 * s2 + 1]);
+            sd[t * (kSDT / 16) + 64 * s2] = sb[t];  // the fp16 S before the chunk, for the read-out
+        }
 #pragma unroll
         for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -181,15 +186,6 @@ __device__ __forceinline__ void state_chunk(const unsigned char *smem, floatx4 (
                               (_Float16)(d[2 * s + 1][2] * c1.z), (_Float16)(d[2 * s + 1][3] * c1.w)};
         }
     }
-    // (S is packed afresh here: keeping the K S loop's packed copy alive until now would
-    // cost 8 NT registers, so the compiler is kept from reusing it)
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-            asm volatile("" : "+v"(S[t][2 * s2]), "+v"(S[t][2 * s2 + 1]));
-            sd[t * (kSDT / 16) + 64 * s2] = pack_tiles(S[t][2 * s2], S[t][2 * s2 + 1]);
-        }
     // S = e^{G_C} S + K^T Delta~, each k^T fragment used for every tile, then reloaded.  The
     // token step is the outer loop, so 8 NT independent accumulations separate the two
     // products into one accumulator.
