@@ -5,7 +5,8 @@ The hand-picked cases elsewhere cover the edges one at a time; this sweep draws
 combinations of them: head ratios, ragged lengths, the conv and norm switches,
 random initial states or none, packed batches of random lengths, forced segment
 counts of the two-level scan, and multi-token decode with snapshots.  The draws
-come from one fixed seed, so every run checks the same configurations.
+come from two fixed seeds (the second with more and wider heads), so every run checks
+the same configurations.
 """
 import os
 
@@ -44,7 +45,24 @@ def _configs(n=12):
     return out
 
 
-CONFIGS = _configs()
+def _wide_configs(n=24):
+    # wider draws: up to 8 key heads and 4 value heads per key head, so that B Hv crosses 32
+    # (two-tile slices) and the sequential pass runs more items than one round of workgroups
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([GI.SEED_BASE, 1777])))
+    out = []
+    for i in range(n):
+        Hk = int(rng.choice([1, 2, 4, 8]))
+        r = int(rng.choice([1, 2, 3, 4]))
+        out.append(dict(
+            i=100 + i, Hk=Hk, Hv=Hk * r, B=int(rng.integers(1, 5)), T=int(rng.integers(1, 700)),
+            conv=bool(rng.random() < 0.8), norm=bool(rng.random() < 0.8), rs=bool(rng.random() < 0.6),
+            nseg=int(rng.choice([0, 0, 2, 3, 5])),
+            lengths=[int(x) for x in rng.integers(1, 300, size=int(rng.integers(1, 7)))],
+            Tdec=int(rng.integers(1, 9))))
+    return out
+
+
+CONFIGS = _configs() + _wide_configs()
 
 
 def _ids(c):
